@@ -1,0 +1,154 @@
+/*
+ * lce.h - strip-wise linear cross-entropy on AMD CDNA4 (gfx950).
+ *
+ * Computes loss = CE(h . W^T, targets) and its gradients for hidden states
+ * h [N, H] and a projection weight W [V, H] without ever holding the N x V
+ * logits.  This is the loss primitive that the page "Running 128K-Sequence MoE
+ * RL on 32 H100s" calls Linear CE (section "Linear CE: Avoiding
+ * Materialization of Full Logits"), computed the way the page "Flattening
+ * Every Memory Peak in Long-Context Mixture-of-Experts Training" describes for
+ * Ring-DTP on one device's share (section 3.2 and appendix C): each logit strip
+ * h . W[v0:v0+Vs]^T is folded into a running per-token state (max, sum of
+ * exponentials, target logit) and released; the backward pass recomputes each
+ * strip, forms G = grad_scale * (softmax - onehot) for it, and feeds
+ * dH += G . W_strip and dW_strip = G^T . h.  Section 2 of the second page
+ * fixes the contract: forward values and gradients equal those of the dense
+ * implementation up to the order of floating-point operations.
+ *
+ * Conventions for every call
+ *  - All tensors are dense row-major and live in device memory, unless stated.
+ *    hidden [N, H] and weight rows [*, H] have the element type of `dtype`;
+ *    targets are int32 [N]; every float output is float32.
+ *  - Device pointers must be 16-byte aligned.  H must be a multiple of 8 for
+ *    bf16 and of 4 for f32 (LCE_ERR_UNSUPPORTED otherwise).
+ *  - The library never allocates device memory.  The caller passes a
+ *    workspace of at least lce_workspace_bytes(p) bytes; it is scratch, its
+ *    contents are not kept between calls, and two calls that run at the same
+ *    time need two workspaces.
+ *  - Work is enqueued on `stream` and is asynchronous: no call waits for the
+ *    device.  Argument errors are detected on the host and returned before
+ *    anything is enqueued.  A failed kernel launch returns LCE_ERR_LAUNCH.
+ *  - A non-ignored target outside [0, V) is a precondition violation: the
+ *    kernels stay memory-safe (targets are compared, never used as
+ *    addresses) and that row's loss, and so the reduced loss, is NaN.
+ */
+#ifndef LCE_H
+#define LCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lce_status {
+  LCE_OK = 0,
+  LCE_ERR_INVALID_VALUE = 1, /* null pointer, size <= 0, bad enum, strip range */
+  LCE_ERR_UNSUPPORTED = 2,   /* H not a multiple of the 16-byte chunk */
+  LCE_ERR_WORKSPACE = 3,     /* workspace null or smaller than lce_workspace_bytes */
+  LCE_ERR_LAUNCH = 4         /* a kernel launch failed (hipGetLastError) */
+} lce_status_t;
+
+typedef enum lce_dtype { LCE_F32 = 0, LCE_BF16 = 1 } lce_dtype_t;
+
+typedef enum lce_reduction {
+  LCE_MEAN = 0, /* sum of row losses / number of non-ignored rows (NaN if none) */
+  LCE_SUM = 1   /* sum of row losses */
+} lce_reduction_t;
+
+/* The problem: sizes, element type, reduction and strip width.
+ * strip (Vs) is the widest vocabulary slice folded per step; it fixes the
+ * workspace size.  0 selects lce_pick_strip(p, LCE_DEFAULT_BUDGET). */
+typedef struct lce_problem {
+  int64_t n_tokens;     /* N >= 1 */
+  int64_t hidden;       /* H >= 1 */
+  int64_t vocab;        /* V >= 1 */
+  int64_t strip;        /* Vs in [1, V], or 0 */
+  int32_t dtype;        /* lce_dtype_t of hidden and weight */
+  int32_t reduction;    /* lce_reduction_t */
+  int32_t ignore_index; /* rows with this target are left out */
+  int32_t reserved;     /* must be 0 */
+} lce_problem_t;
+
+#define LCE_DEFAULT_BUDGET ((size_t)2 << 30) /* 2 GiB of workspace */
+
+/* Human-readable name of a status code (static storage). */
+const char* lce_status_string(lce_status_t s);
+
+/* Widest strip width Vs whose workspace fits in budget_bytes: a multiple of
+ * 256 (the kernels' vocabulary tile), at least 256, at most V rounded up to
+ * 256, then clamped to V.  Follows from the second page's section 3.5 (device
+ * working sets fixed by the launch configuration, checkable before launch).
+ * Returns -1 for an invalid problem. p->strip is ignored. */
+int64_t lce_pick_strip(const lce_problem_t* p, size_t budget_bytes);
+
+/* Workspace bytes needed by every call below for problem p (with its strip,
+ * or the default policy when p->strip == 0): one gradient strip
+ * N x round_up(Vs, 256) elements plus 12 bytes per token and a small header.
+ * Returns 0 for an invalid problem. */
+size_t lce_workspace_bytes(const lce_problem_t* p);
+
+/* Forward: loss[0] (float32, device), lse[N] (log-sum-exp of every row,
+ * needed by lce_backward) and, if row_loss != NULL, row_loss[N] (0 for
+ * ignored rows).  Strips are folded in natural order 0, Vs, 2Vs, ...
+ * Equivalent to lce_forward_begin + one lce_forward_fold per strip +
+ * lce_forward_end. */
+lce_status_t lce_forward(const lce_problem_t* p, const void* hidden, const void* weight,
+                         const int32_t* targets, float* loss, float* lse, float* row_loss,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward: d_hidden [N, H] and d_weight [V, H] (float32, fully overwritten)
+ * of grad_out[0] * loss.  lse is the forward's output; grad_out is a device
+ * scalar.  Ignored rows get zero d_hidden rows and add nothing to d_weight.
+ * Equivalent to lce_backward_begin + one lce_backward_fold per strip. */
+lce_status_t lce_backward(const lce_problem_t* p, const void* hidden, const void* weight,
+                          const int32_t* targets, const float* lse, const float* grad_out,
+                          float* d_hidden, float* d_weight, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Strip-level calls: the caller chooses the strips and their order ----
+ * One fold is one meeting of the token batch with one vocabulary shard in the
+ * second page's Ring-DTP (appendix C): any order that visits every vocabulary
+ * row exactly once gives the same result up to rounding.  weight_strip points
+ * at row v_begin of the weight (v_len rows of H elements), 1 <= v_len <= Vs
+ * and 0 <= v_begin, v_begin + v_len <= V. */
+
+/* Reset the running per-token state (max = -inf, sum = 0, target logit = NaN). */
+lce_status_t lce_forward_begin(const lce_problem_t* p, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Fold the logits of vocabulary rows [v_begin, v_begin + v_len) into the state. */
+lce_status_t lce_forward_fold(const lce_problem_t* p, const void* hidden,
+                              const void* weight_strip, int64_t v_begin, int64_t v_len,
+                              const int32_t* targets, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Turn the state into lse[N], optional row_loss[N] and the reduced loss[0]. */
+lce_status_t lce_forward_end(const lce_problem_t* p, const int32_t* targets, float* loss,
+                             float* lse, float* row_loss, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Count the non-ignored rows and form the per-row gradient scale from the
+ * device scalar grad_out (grad_out / n_valid for mean, grad_out for sum). */
+lce_status_t lce_backward_begin(const lce_problem_t* p, const int32_t* targets,
+                                const float* grad_out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* Recompute the strip, form its logit gradient G in the workspace, then
+ * d_hidden = G . W_strip (accumulate == 0) or d_hidden += G . W_strip
+ * (accumulate != 0), and d_weight_strip[v_len, H] = G^T . h (overwritten).
+ * The first fold of a backward pass must pass accumulate = 0. */
+lce_status_t lce_backward_fold(const lce_problem_t* p, const void* hidden,
+                               const void* weight_strip, int64_t v_begin, int64_t v_len,
+                               const int32_t* targets, const float* lse, float* d_hidden,
+                               int accumulate, float* d_weight_strip, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H */

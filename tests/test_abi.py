@@ -1,0 +1,116 @@
+"""The C ABI of liblce.so on the host (CPU only, nothing is launched).
+
+Checks that the library loads, exports every function include/lce.h declares,
+and rejects bad arguments before enqueuing anything.  Also checks the
+strip-width policy and the workspace size formula.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from vocab_projection_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lce.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lce_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("liblce.so is not built (python -m vocab_projection_amd.build)")
+    return B.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(B.EXPORTS)
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["LCE_OK", "LCE_ERR_INVALID_VALUE", "LCE_ERR_UNSUPPORTED",
+                                 "LCE_ERR_WORKSPACE", "LCE_ERR_LAUNCH"]):
+        assert lib.lce_status_string(code).decode() == name
+
+
+def P(n=64, h=64, v=1000, dtype=torch.bfloat16, **kw):
+    return B.problem(n, h, v, dtype, **kw)
+
+
+def test_workspace_formula(lib):
+    p = P(131072, 2048, 151936, strip=8192)
+    col = (4 * 131072 + 255) // 256 * 256
+    assert B.lce_workspace_bytes(p) == 256 + 3 * col + 131072 * 8192 * 2
+    p = P(256, 128, 1024, torch.float32, strip=256)
+    assert B.lce_workspace_bytes(p) == 256 + 3 * 1024 + 256 * 256 * 4
+    p = P(100, 64, 1000, strip=300)  # strip buffer rounds the strip up to 256 columns
+    assert B.lce_workspace_bytes(p) == 256 + 3 * 512 + 100 * 512 * 2
+
+
+def test_pick_strip_policy(lib):
+    n = 131072
+    p = P(n, 2048, 151936)
+    fixed = 256 + 3 * ((4 * n + 255) // 256 * 256)
+    vs = B.lce_pick_strip(p, fixed + n * 2 * 8192)
+    assert vs == 8192
+    assert B.lce_pick_strip(p, fixed + n * 2 * 8192 - 1) == 8192 - 256
+    assert B.lce_pick_strip(p, 0) == 256          # floor: one tile
+    assert B.lce_pick_strip(p, 1 << 50) == 151936  # ceiling: the whole vocabulary
+    for budget in (1 << 28, 1 << 30, 3 << 30):
+        vs = B.lce_pick_strip(p, budget)
+        p2 = P(n, 2048, 151936, strip=vs)
+        assert B.lce_workspace_bytes(p2) <= budget
+        assert vs % 256 == 0
+    bad = P(0, 64, 10)
+    assert B.lce_pick_strip(bad, 1 << 20) == -1
+
+
+def test_problem_validation(lib):
+    assert lib.lce_workspace_bytes(ctypes.byref(P(0))) == 0
+    assert lib.lce_workspace_bytes(ctypes.byref(P(v=0))) == 0
+    assert lib.lce_workspace_bytes(ctypes.byref(P(strip=1001))) == 0
+    p = P()
+    p.dtype = 7
+    assert lib.lce_workspace_bytes(ctypes.byref(p)) == 0
+    p = P()
+    p.reduction = 5
+    assert lib.lce_workspace_bytes(ctypes.byref(p)) == 0
+    assert lib.lce_workspace_bytes(ctypes.byref(P(h=12))) == 0          # bf16 needs H % 8 == 0
+    assert lib.lce_workspace_bytes(ctypes.byref(P(h=12, dtype=torch.float32))) > 0
+
+
+def _call_fwd(lib, p, ws_bytes, ptrs):
+    return lib.lce_forward(ctypes.byref(p), *ptrs[:6], ptrs[6], ws_bytes, None)
+
+
+def test_errors_are_returned_before_any_launch(lib):
+    p = P()
+    need = B.lce_workspace_bytes(p)
+    fake = 0x10000  # aligned, never dereferenced: every call below fails its checks first
+    ok = [fake] * 7
+    assert _call_fwd(lib, p, need - 1, ok) == 3                      # workspace too small
+    assert _call_fwd(lib, p, need, [fake, None] + [fake] * 5) == 1  # null weight
+    assert _call_fwd(lib, p, need, [fake + 2] + [fake] * 6) == 1     # misaligned hidden
+    assert _call_fwd(lib, p, need, [fake] * 6 + [None]) == 3         # null workspace
+    assert _call_fwd(lib, P(h=12), need, ok) == 2                    # unsupported H
+    assert _call_fwd(lib, P(n=-1), need, ok) == 1
+    assert lib.lce_forward_fold(ctypes.byref(p), fake, fake, 990, 20, fake, fake, need, None) == 1
+    assert lib.lce_forward_fold(ctypes.byref(p), fake, fake, 0, 0, fake, fake, need, None) == 1
+    p.strip = 256
+    need = B.lce_workspace_bytes(p)
+    assert lib.lce_forward_fold(ctypes.byref(p), fake, fake, 0, 257, fake, fake, need, None) == 1
+    assert lib.lce_backward_fold(ctypes.byref(p), fake, fake, 0, 10, fake, None, fake, 0, fake,
+                                 fake, need, None) == 1
+    assert lib.lce_backward(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, need,
+                            None) == 1

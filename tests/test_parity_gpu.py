@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small problems (several tiles, ragged N, H and V) are checked element by
+element against the full oracle.  The five workloads at full size run in the
+same launch configuration as the benchmark and are checked on the exact loss
+and every row's lse (stored oracle results, tests/golden/), on sampled rows of
+dH (oracle per row) and sampled vocabulary rows of dW (oracle per column,
+with the stored lse), plus invariants that hold at any size.
+
+Tolerances (float32 inputs): |dloss|/loss <= 1e-5 and, per gradient tensor,
+max|diff| / max|ref| <= 1e-4.  bf16 inputs: |dloss|/loss <= 2e-3 and, per
+gradient tensor, ||diff||_F / ||ref||_F <= 1e-2.  lse is checked at
+|dlse| <= 2e-5 * (1 + |lse|): logits are exact bf16 products summed in fp32,
+so lse carries only fp32 rounding.
+"""
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lce_oracle as O
+from vocab_projection_amd import binding as B
+from vocab_projection_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def torch_dtype(w):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def to_gpu(w, hid, wt, t):
+    dt = torch_dtype(w)
+    return (torch.from_numpy(hid).to(DEV).to(dt).contiguous(),
+            torch.from_numpy(wt).to(DEV).to(dt).contiguous(),
+            torch.from_numpy(t).to(DEV))
+
+
+def run_hip(w, h, W, t, *, strip=None, order=None, grad_out=None):
+    """Forward + backward through the C ABI; order=None uses lce_forward/lce_backward,
+    otherwise the strip-level calls in the given (v_begin, v_len) order."""
+    vs = strip or w.strip
+    p = B.make_problem(h, W, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, strip=vs)
+    ws = B.workspace(p, DEV)
+    go = torch.tensor([w.grad_out if grad_out is None else grad_out], dtype=torch.float32,
+                      device=DEV)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    lse = torch.empty(h.shape[0], dtype=torch.float32, device=DEV)
+    row_loss = torch.empty_like(lse)
+    dh = torch.empty(h.shape, dtype=torch.float32, device=DEV)
+    dw = torch.empty(W.shape, dtype=torch.float32, device=DEV)
+    if order is None:
+        B.lce_forward(p, h, W, t, loss, lse, row_loss, ws)
+        B.lce_backward(p, h, W, t, lse, go, dh, dw, ws)
+    else:
+        B.lce_forward_begin(p, ws)
+        for v0, vl in order:
+            B.lce_forward_fold(p, h, W[v0:v0 + vl], v0, vl, t, ws)
+        B.lce_forward_end(p, t, loss, lse, row_loss, ws)
+        B.lce_backward_begin(p, t, go, ws)
+        for k, (v0, vl) in enumerate(order):
+            B.lce_backward_fold(p, h, W[v0:v0 + vl], v0, vl, t, lse, dh, k > 0, dw[v0:v0 + vl], ws)
+    torch.cuda.synchronize()
+    return dict(loss=loss.item(), lse=lse.cpu().numpy(), row_loss=row_loss.cpu().numpy(),
+                dh=dh, dw=dw)
+
+
+def assert_loss(w, got, ref):
+    tol = 1e-5 if w.dtype == "f32" else 2e-3
+    assert abs(got - ref) <= tol * abs(ref), (got, ref)
+
+
+def assert_grad(w, got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(got)), what
+    if w.dtype == "f32":
+        err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+        assert err <= 1e-4, (what, err)
+    else:
+        err = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+        assert err <= 1e-2, (what, err)
+    return err
+
+
+def assert_lse(got, ref):
+    ref = np.asarray(ref)
+    err = np.abs(np.asarray(got, dtype=np.float64) - ref) / (1.0 + np.abs(ref))
+    assert err.max() <= 2e-5, err.max()
+
+
+def full_check(w, strip=None, order=None):
+    hid, wt, t = S.hidden(w), S.weight(w), S.targets(w)
+    h, W, tt = to_gpu(w, hid, wt, t)
+    out = run_hip(w, h, W, tt, strip=strip, order=order)
+    loss, lse, row_loss = O.forward(hid, wt, t, ignore_index=S.IGNORE_INDEX, reduction=w.reduction)
+    dh, dw = O.backward(hid, wt, t, ignore_index=S.IGNORE_INDEX, reduction=w.reduction,
+                        grad_out=w.grad_out)
+    assert_loss(w, out["loss"], loss)
+    assert_lse(out["lse"], lse)
+    np.testing.assert_allclose(out["row_loss"], row_loss, rtol=1e-4, atol=1e-3)
+    e1 = assert_grad(w, out["dh"].cpu().numpy(), dh, "dH")
+    e2 = assert_grad(w, out["dw"].cpu().numpy(), dw, "dW")
+    say(f"{w.name}: loss {out['loss']:.6f} vs {loss:.6f}; dH err {e1:.2e}; dW err {e2:.2e}")
+    return out
+
+
+SMALL = [
+    S.Workload("tiny_f32", 256, 128, 1024, 256, "f32", 1.0, 1 / math.sqrt(128), "uniform"),
+    S.small("bf16_ragged", 1000, 200, 3001, 1024, ignore_frac=0.1),
+    S.small("bf16_ragged_sum", 517, 64, 2000, 512, reduction="sum", grad_out=0.37,
+            target_law="zipf"),
+    S.small("f32_ragged", 300, 132, 777, 256, "f32", weight_std=0.2, ignore_frac=0.05),
+    S.small("bf16_one_strip", 333, 96, 700, 700),
+    S.small("bf16_tiny_strip", 64, 32, 50, 8),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_full_parity(w):
+    full_check(S.WORKLOADS["tiny_f32"] if w.name == "tiny_f32" else w)
+
+
+def test_strip_width_and_fold_order_invariance():
+    w = S.small("bf16_invariance", 640, 128, 2600, 1024, ignore_frac=0.1, shards=4, ring_start=3)
+    hid, wt, t = S.hidden(w), S.weight(w), S.targets(w)
+    h, W, tt = to_gpu(w, hid, wt, t)
+    base = run_hip(w, h, W, tt, strip=256)
+    for strip, order in ((1024, None), (2600, None), (1024, S.fold_order(w))):
+        o = run_hip(w, h, W, tt, strip=strip, order=order)
+        assert abs(o["loss"] - base["loss"]) <= 1e-5 * abs(base["loss"])
+        np.testing.assert_allclose(o["lse"], base["lse"], rtol=1e-6, atol=1e-5)
+        for k in ("dh", "dw"):
+            a, b = o[k].cpu().numpy(), base[k].cpu().numpy()
+            assert np.linalg.norm(a - b) <= 1e-3 * np.linalg.norm(b)
+    full_check(w, strip=1024, order=S.fold_order(w))
+
+
+def test_deterministic():
+    w = S.small("bf16_det", 700, 128, 3000, 1024, ignore_frac=0.1)
+    h, W, tt = to_gpu(w, S.hidden(w), S.weight(w), S.targets(w))
+    a = run_hip(w, h, W, tt)
+    b = run_hip(w, h, W, tt)
+    assert a["loss"] == b["loss"]
+    assert np.array_equal(a["lse"], b["lse"])
+    assert torch.equal(a["dh"], b["dh"]) and torch.equal(a["dw"], b["dw"])
+
+
+def test_zero_weight_gives_log_vocab():
+    w = S.small("bf16_zero_w", 300, 64, 1500, 512, ignore_frac=0.2)
+    hid, t = S.hidden(w), S.targets(w)
+    h, W, tt = to_gpu(w, hid, np.zeros((w.vocab, w.hidden), np.float32), t)
+    o = run_hip(w, h, W, tt)
+    assert abs(o["loss"] - math.log(w.vocab)) <= 1e-6 * math.log(w.vocab)
+    np.testing.assert_allclose(o["lse"], math.log(w.vocab), rtol=1e-6)
+    assert torch.count_nonzero(o["dh"]).item() == 0
+    sc = O.grad_scale(t, ignore_index=S.IGNORE_INDEX, reduction="mean", grad_out=1.0)
+    closed = np.zeros((w.vocab, w.hidden))
+    closed += (sc[:, None] * hid).sum(axis=0)[None, :] / w.vocab
+    valid = t != S.IGNORE_INDEX
+    np.add.at(closed, t[valid], -sc[valid, None] * hid[valid])
+    assert_grad(w, o["dw"].cpu().numpy(), closed, "dW closed form")
+
+
+def test_large_logits_are_stable():
+    """Logits near +-100 (std about 20) overflow an unshifted fp32 exp."""
+    w = S.small("bf16_hot", 256, 256, 4096, 1024, weight_std=20 / 16.0, target_law="zipf",
+                ignore_frac=0.05)
+    full_check(w)
+
+
+def test_all_rows_ignored_and_single_row():
+    w = S.small("bf16_all_ignored", 40, 64, 600, 256, ignore_frac=1.0)
+    h, W, tt = to_gpu(w, S.hidden(w), S.weight(w), S.targets(w))
+    o = run_hip(w, h, W, tt)
+    assert math.isnan(o["loss"])
+    assert torch.count_nonzero(o["dh"]).item() == 0 and torch.count_nonzero(o["dw"]).item() == 0
+    w1 = S.small("bf16_one_row", 1, 8, 1, 1)
+    o1 = full_check(w1)
+    assert abs(o1["loss"]) < 1e-6  # a single vocabulary row: softmax is 1, loss 0
+
+
+def test_out_of_range_target_gives_nan_loss():
+    w = S.small("bf16_bad_target", 64, 64, 500, 256)
+    t = S.targets(w)
+    t[3] = 500
+    h, W, tt = to_gpu(w, S.hidden(w), S.weight(w), t)
+    o = run_hip(w, h, W, tt)
+    assert math.isnan(o["loss"]) and math.isnan(o["row_loss"][3])
+
+
+def test_autograd_function():
+    w = S.small("bf16_autograd", 200, 64, 900, 256, ignore_frac=0.1)
+    hid, wt, t = S.hidden(w), S.weight(w), S.targets(w)
+    h, W, tt = to_gpu(w, hid, wt, t)
+    h32 = h.float().requires_grad_(True)
+    W32 = W.float().requires_grad_(True)
+    loss = B.LinearCrossEntropy.apply(h32, W32, tt, S.IGNORE_INDEX, "mean", 256)
+    (2.0 * loss).backward()
+    dh, dw = O.backward(hid, wt, t, ignore_index=S.IGNORE_INDEX, grad_out=2.0)
+    assert_grad(S.small("f", 1, 1, 1, 1, "f32"), h32.grad.cpu().numpy(), dh, "dH")
+    assert_grad(S.small("f", 1, 1, 1, 1, "f32"), W32.grad.cpu().numpy(), dw, "dW")
+
+
+# ------------------------- full-size workloads -------------------------
+
+def sample_rows(w, t, rng, k):
+    n = w.n_tokens
+    ign = np.nonzero(t == S.IGNORE_INDEX)[0]
+    hot = np.nonzero(t == 0)[0]
+    picks = [0, n - 1, n // 2]
+    picks += list(ign[:8]) + list(hot[:8])
+    picks += list(rng.choice(n, size=k - len(picks), replace=False))
+    return np.unique(np.array(picks, dtype=np.int64))
+
+
+def sample_vocab(w, t, rng, k):
+    v = w.vocab
+    picks = list(range(16)) + [v - 1, v - 2]
+    picks += [b for a in range(0, v, w.strip) for b in (a - 1, a) if 0 <= b < v][:32]
+    valid_t = t[t != S.IGNORE_INDEX]
+    picks += list(valid_t[:16])
+    picks += list(rng.choice(v, size=max(0, k - len(picks)), replace=False))
+    return np.unique(np.array(picks, dtype=np.int64))[:k]
+
+
+@pytest.mark.parametrize("name", [n for n in S.WORKLOAD_ORDER if n != "tiny_f32"])
+def test_full_size_sampled(name):
+    w = S.WORKLOADS[name]
+    gpath = os.path.join(GOLDEN, f"{name}.npz")
+    if not os.path.exists(gpath):
+        pytest.skip(f"stored oracle results {gpath} not generated yet")
+    g = np.load(gpath)
+    t0 = time.time()
+    hid, wt, t = S.hidden(w, threads=16), S.weight(w, threads=16), S.targets(w)
+    fv = np.concatenate([hid[[0, -1], :8].ravel(), wt[[0, -1], :8].ravel()])
+    assert np.array_equal(fv, g["fp_values"]), "generated inputs differ from the stored ones"
+    say(f"{name}: inputs {time.time() - t0:.1f}s")
+    h, W, tt = to_gpu(w, hid, wt, t)
+    order = S.fold_order(w) if w.shards else None
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    out = run_hip(w, h, W, tt, order=order)
+    peak_extra = torch.cuda.max_memory_allocated() - base
+    p = B.make_problem(h, W, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, strip=w.strip)
+    ws_bytes = B.lce_workspace_bytes(p)
+    outputs = 4 * (w.n_tokens * (3 + w.hidden) + w.vocab * w.hidden) + 4
+    say(f"{name}: gpu done {time.time() - t0:.1f}s; peak extra {peak_extra / 1e9:.3f} GB "
+        f"(workspace {ws_bytes / 1e9:.3f} GB, full logits {w.n_tokens * w.vocab * 2 / 1e9:.2f} GB)")
+    assert peak_extra <= ws_bytes + outputs + (64 << 20)
+    assert ws_bytes < 1.02 * w.n_tokens * w.strip * w.elt_bytes + (1 << 20)
+
+    assert_loss(w, out["loss"], float(g["loss"]))
+    assert_lse(out["lse"], g["lse"])
+    rng = np.random.default_rng(99)
+    rows = sample_rows(w, t, rng, 256)
+    vids = sample_vocab(w, t, rng, 256)
+    sc = O.grad_scale(t, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, grad_out=w.grad_out)
+    ref_dh = O.hidden_grad_rows(hid[rows], wt, t[rows], sc[rows])
+    e1 = assert_grad(w, out["dh"][torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref_dh, "dH rows")
+    say(f"{name}: dH rows checked {time.time() - t0:.1f}s err {e1:.2e}")
+    ref_dw = O.weight_grad_rows(hid, wt[vids], vids, t, g["lse"], sc)
+    e2 = assert_grad(w, out["dw"][torch.from_numpy(vids).to(DEV)].cpu().numpy(), ref_dw, "dW rows")
+    say(f"{name}: dW rows checked {time.time() - t0:.1f}s err {e2:.2e}")
+    # invariants at full size
+    ign = torch.from_numpy(np.nonzero(t == S.IGNORE_INDEX)[0]).to(DEV)
+    if ign.numel():
+        assert torch.count_nonzero(out["dh"][ign]).item() == 0
+    colsum = out["dw"].double().sum(dim=0)
+    assert colsum.norm().item() <= 1e-2 * out["dw"].double().norm().item()

@@ -1,0 +1,313 @@
+// lce_api.cpp - the C ABI of include/lce.h: argument checks, the strip-width
+// policy, the workspace carve and the strip loop.  Every call only enqueues
+// kernels on the caller's stream; nothing here waits for the device or
+// allocates device memory.
+#include "lce.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "lce_kernels.h"
+
+namespace {
+
+constexpr int64_t kStripTile = 256;  // vocabulary tile of the strip kernels
+constexpr int64_t kPartRows = 128;   // vocabulary rows per forward partial
+constexpr size_t kHeader = 256;
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+struct Plan {
+  int64_t N, H, V, Vs, ldg;
+  int dtype, reduction;
+  int32_t ignore_index;
+  size_t elt;
+  size_t off_m, off_s, off_zt, off_strip, total;
+};
+
+bool problem_ok(const lce_problem_t* p) {
+  if (!p) return false;
+  if (p->n_tokens < 1 || p->hidden < 1 || p->vocab < 1) return false;
+  if (p->strip < 0 || p->strip > p->vocab) return false;
+  if (p->dtype != LCE_F32 && p->dtype != LCE_BF16) return false;
+  if (p->reduction != LCE_MEAN && p->reduction != LCE_SUM) return false;
+  if (p->reserved != 0) return false;
+  // keep every index and byte offset far inside int64
+  if (p->n_tokens > (1LL << 31) || p->hidden > (1LL << 24) || p->vocab > (1LL << 31)) return false;
+  return true;
+}
+
+size_t elt_of(int dtype) { return dtype == LCE_BF16 ? 2 : 4; }
+
+size_t fixed_bytes(int64_t n) {
+  return kHeader + 3 * (size_t)round_up(4 * n, 256);
+}
+
+size_t bytes_for_strip(int64_t n, int64_t vs, size_t elt) {
+  const int64_t ldg = round_up(vs, kStripTile);
+  const size_t g = (size_t)n * (size_t)ldg * elt;                   // backward G strip
+  const size_t part = (size_t)n * (size_t)(ldg / kPartRows) * 8;    // forward partials
+  return fixed_bytes(n) + (g > part ? g : part);
+}
+
+int64_t pick_strip(const lce_problem_t* p, size_t budget) {
+  const size_t elt = elt_of(p->dtype);
+  const int64_t n = p->n_tokens;
+  const int64_t vmax = round_up(p->vocab, kStripTile);
+  int64_t vs = kStripTile;
+  const size_t fixed = fixed_bytes(n);
+  if (budget > fixed) {
+    const size_t per_tile = (size_t)n * (size_t)kStripTile * elt;
+    const int64_t tiles = (int64_t)((budget - fixed) / per_tile);
+    if (tiles * kStripTile > vs) vs = tiles * kStripTile;
+  }
+  if (vs > vmax) vs = vmax;
+  if (vs > p->vocab) vs = p->vocab;
+  return vs;
+}
+
+lce_status_t make_plan(const lce_problem_t* p, Plan* pl) {
+  if (!problem_ok(p)) return LCE_ERR_INVALID_VALUE;
+  const size_t elt = elt_of(p->dtype);
+  if ((p->hidden * (int64_t)elt) % 16 != 0) return LCE_ERR_UNSUPPORTED;
+  pl->N = p->n_tokens;
+  pl->H = p->hidden;
+  pl->V = p->vocab;
+  pl->Vs = p->strip ? p->strip : pick_strip(p, LCE_DEFAULT_BUDGET);
+  pl->ldg = round_up(pl->Vs, kStripTile);
+  pl->dtype = p->dtype;
+  pl->reduction = p->reduction;
+  pl->ignore_index = p->ignore_index;
+  pl->elt = elt;
+  const size_t col = (size_t)round_up(4 * pl->N, 256);
+  pl->off_m = kHeader;
+  pl->off_s = pl->off_m + col;
+  pl->off_zt = pl->off_s + col;
+  pl->off_strip = pl->off_zt + col;
+  pl->total = bytes_for_strip(pl->N, pl->Vs, elt);
+  return LCE_OK;
+}
+
+bool aligned(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+lce_status_t check_ws(const Plan& pl, void* ws, size_t ws_bytes) {
+  if (!ws || !aligned(ws)) return LCE_ERR_WORKSPACE;
+  if (ws_bytes < pl.total) return LCE_ERR_WORKSPACE;
+  return LCE_OK;
+}
+
+lce_status_t launched(hipError_t e) { return e == hipSuccess ? LCE_OK : LCE_ERR_LAUNCH; }
+
+struct Carve {
+  lce::Control* ctrl;
+  float *m, *s, *zt;
+  char* strip;
+};
+
+Carve carve(const Plan& pl, void* ws) {
+  char* b = static_cast<char*>(ws);
+  return Carve{reinterpret_cast<lce::Control*>(b), reinterpret_cast<float*>(b + pl.off_m),
+               reinterpret_cast<float*>(b + pl.off_s), reinterpret_cast<float*>(b + pl.off_zt),
+               b + pl.off_strip};
+}
+
+lce_status_t check_strip(const Plan& pl, const void* weight_strip, int64_t v_begin,
+                         int64_t v_len) {
+  if (!weight_strip || !aligned(weight_strip)) return LCE_ERR_INVALID_VALUE;
+  if (v_len < 1 || v_len > pl.Vs || v_begin < 0 || v_begin > pl.V - v_len)
+    return LCE_ERR_INVALID_VALUE;
+  return LCE_OK;
+}
+
+template <typename T>
+lce_status_t fold_fwd(const Plan& pl, const void* hidden, const void* weight_strip,
+                      int64_t v_begin, int64_t v_len, const int32_t* targets, void* ws,
+                      hipStream_t st) {
+  Carve c = carve(pl, ws);
+  lce::StripArgs<T> a{};
+  a.hidden = static_cast<const T*>(hidden);
+  a.weight_strip = static_cast<const T*>(weight_strip);
+  a.targets = targets;
+  a.N = pl.N;
+  a.H = pl.H;
+  a.v_begin = v_begin;
+  a.v_len = v_len;
+  a.ignore_index = pl.ignore_index;
+  a.partials = reinterpret_cast<float2*>(c.strip);
+  a.z_target = c.zt;
+  lce_status_t s = launched(lce::launch_strip_lse<T>(a, st));
+  if (s != LCE_OK) return s;
+  const int64_t nblk = (v_len + kPartRows - 1) / kPartRows;
+  return launched(lce::launch_fold(a.partials, nblk, c.m, c.s, pl.N, st));
+}
+
+template <typename T>
+lce_status_t fold_bwd(const Plan& pl, const void* hidden, const void* weight_strip,
+                      int64_t v_begin, int64_t v_len, const int32_t* targets, const float* lse,
+                      float* d_hidden, int accumulate, float* d_weight_strip, void* ws,
+                      hipStream_t st) {
+  Carve c = carve(pl, ws);
+  lce::StripArgs<T> a{};
+  a.hidden = static_cast<const T*>(hidden);
+  a.weight_strip = static_cast<const T*>(weight_strip);
+  a.targets = targets;
+  a.N = pl.N;
+  a.H = pl.H;
+  a.v_begin = v_begin;
+  a.v_len = v_len;
+  a.ignore_index = pl.ignore_index;
+  a.lse = lse;
+  a.ctrl = c.ctrl;
+  a.g_strip = reinterpret_cast<T*>(c.strip);
+  a.ldg = pl.ldg;
+  lce_status_t s = launched(lce::launch_strip_grad<T>(a, st));
+  if (s != LCE_OK) return s;
+  s = launched(lce::launch_dh<T>(a.g_strip, pl.ldg, a.weight_strip, v_len, pl.N, pl.H, d_hidden,
+                                 accumulate, st));
+  if (s != LCE_OK) return s;
+  return launched(lce::launch_dw<T>(a.g_strip, pl.ldg, a.hidden, v_len, pl.N, pl.H,
+                                    d_weight_strip, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lce_status_string(lce_status_t s) {
+  switch (s) {
+    case LCE_OK: return "LCE_OK";
+    case LCE_ERR_INVALID_VALUE: return "LCE_ERR_INVALID_VALUE";
+    case LCE_ERR_UNSUPPORTED: return "LCE_ERR_UNSUPPORTED";
+    case LCE_ERR_WORKSPACE: return "LCE_ERR_WORKSPACE";
+    case LCE_ERR_LAUNCH: return "LCE_ERR_LAUNCH";
+  }
+  return "LCE_ERR_UNKNOWN";
+}
+
+int64_t lce_pick_strip(const lce_problem_t* p, size_t budget_bytes) {
+  if (!problem_ok(p)) return -1;
+  return pick_strip(p, budget_bytes);
+}
+
+size_t lce_workspace_bytes(const lce_problem_t* p) {
+  Plan pl;
+  if (make_plan(p, &pl) != LCE_OK) return 0;
+  return pl.total;
+}
+
+lce_status_t lce_forward_begin(const lce_problem_t* p, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
+  Carve c = carve(pl, ws);
+  return launched(lce::launch_state_init(c.m, c.s, c.zt, pl.N, stream));
+}
+
+lce_status_t lce_forward_fold(const lce_problem_t* p, const void* hidden,
+                              const void* weight_strip, int64_t v_begin, int64_t v_len,
+                              const int32_t* targets, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
+  if (!hidden || !aligned(hidden) || !targets) return LCE_ERR_INVALID_VALUE;
+  if ((s = check_strip(pl, weight_strip, v_begin, v_len)) != LCE_OK) return s;
+  return pl.dtype == LCE_BF16
+             ? fold_fwd<__bf16>(pl, hidden, weight_strip, v_begin, v_len, targets, ws, stream)
+             : fold_fwd<float>(pl, hidden, weight_strip, v_begin, v_len, targets, ws, stream);
+}
+
+lce_status_t lce_forward_end(const lce_problem_t* p, const int32_t* targets, float* loss,
+                             float* lse, float* row_loss, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
+  if (!targets || !loss || !lse) return LCE_ERR_INVALID_VALUE;
+  Carve c = carve(pl, ws);
+  return launched(lce::launch_finalize(c.m, c.s, c.zt, targets, pl.N, pl.ignore_index,
+                                       pl.reduction, lse, row_loss, loss, stream));
+}
+
+lce_status_t lce_forward(const lce_problem_t* p, const void* hidden, const void* weight,
+                         const int32_t* targets, float* loss, float* lse, float* row_loss,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
+  if (!hidden || !weight || !targets || !loss || !lse) return LCE_ERR_INVALID_VALUE;
+  if (!aligned(hidden) || !aligned(weight)) return LCE_ERR_INVALID_VALUE;
+  if ((s = lce_forward_begin(p, ws, ws_bytes, stream)) != LCE_OK) return s;
+  const char* w = static_cast<const char*>(weight);
+  for (int64_t v0 = 0; v0 < pl.V; v0 += pl.Vs) {
+    const int64_t len = pl.V - v0 < pl.Vs ? pl.V - v0 : pl.Vs;
+    s = lce_forward_fold(p, hidden, w + (size_t)v0 * pl.H * pl.elt, v0, len, targets, ws,
+                         ws_bytes, stream);
+    if (s != LCE_OK) return s;
+  }
+  return lce_forward_end(p, targets, loss, lse, row_loss, ws, ws_bytes, stream);
+}
+
+lce_status_t lce_backward_begin(const lce_problem_t* p, const int32_t* targets,
+                                const float* grad_out, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
+  if (!targets || !grad_out) return LCE_ERR_INVALID_VALUE;
+  Carve c = carve(pl, ws);
+  return launched(lce::launch_grad_scale(targets, pl.N, pl.ignore_index, pl.reduction, grad_out,
+                                         c.ctrl, stream));
+}
+
+lce_status_t lce_backward_fold(const lce_problem_t* p, const void* hidden,
+                               const void* weight_strip, int64_t v_begin, int64_t v_len,
+                               const int32_t* targets, const float* lse, float* d_hidden,
+                               int accumulate, float* d_weight_strip, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
+  if (!hidden || !aligned(hidden) || !targets || !lse || !d_hidden || !d_weight_strip)
+    return LCE_ERR_INVALID_VALUE;
+  if (!aligned(d_hidden) || !aligned(d_weight_strip)) return LCE_ERR_INVALID_VALUE;
+  if ((s = check_strip(pl, weight_strip, v_begin, v_len)) != LCE_OK) return s;
+  return pl.dtype == LCE_BF16
+             ? fold_bwd<__bf16>(pl, hidden, weight_strip, v_begin, v_len, targets, lse, d_hidden,
+                                accumulate, d_weight_strip, ws, stream)
+             : fold_bwd<float>(pl, hidden, weight_strip, v_begin, v_len, targets, lse, d_hidden,
+                               accumulate, d_weight_strip, ws, stream);
+}
+
+lce_status_t lce_backward(const lce_problem_t* p, const void* hidden, const void* weight,
+                          const int32_t* targets, const float* lse, const float* grad_out,
+                          float* d_hidden, float* d_weight, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
+  if (!hidden || !weight || !targets || !lse || !grad_out || !d_hidden || !d_weight)
+    return LCE_ERR_INVALID_VALUE;
+  if (!aligned(hidden) || !aligned(weight) || !aligned(d_hidden) || !aligned(d_weight))
+    return LCE_ERR_INVALID_VALUE;
+  if ((s = lce_backward_begin(p, targets, grad_out, ws, ws_bytes, stream)) != LCE_OK) return s;
+  const char* w = static_cast<const char*>(weight);
+  for (int64_t v0 = 0; v0 < pl.V; v0 += pl.Vs) {
+    const int64_t len = pl.V - v0 < pl.Vs ? pl.V - v0 : pl.Vs;
+    s = lce_backward_fold(p, hidden, w + (size_t)v0 * pl.H * pl.elt, v0, len, targets, lse,
+                          d_hidden, v0 != 0, d_weight + (size_t)v0 * pl.H, ws, ws_bytes, stream);
+    if (s != LCE_OK) return s;
+  }
+  return LCE_OK;
+}
+
+}  // extern "C"

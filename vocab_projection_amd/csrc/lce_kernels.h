@@ -1,0 +1,64 @@
+// lce_kernels.h - internal launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lce {
+
+// Scalars kept at the head of the workspace.
+struct Control {
+  float grad_scale;   // d loss / d row_loss of a non-ignored row
+  float pad0;
+  long long n_valid;  // non-ignored rows
+};
+
+// One vocabulary strip against all tokens.
+template <typename T>
+struct StripArgs {
+  const T* hidden;        // [N, H]
+  const T* weight_strip;  // [v_len, H], row 0 = vocabulary row v_begin
+  const int32_t* targets; // [N]
+  int64_t N, H;
+  int64_t v_begin, v_len;
+  int32_t ignore_index;
+  int64_t m_tiles;        // set by the launcher
+  // forward
+  float2* partials;       // [ceil(v_len / 128), N]
+  float* z_target;        // [N]
+  // backward
+  const float* lse;       // [N]
+  const Control* ctrl;
+  T* g_strip;             // [N, ldg]
+  int64_t ldg;
+};
+
+template <typename T>
+struct GemmArgs {
+  const T* a; int64_t lda, a_mn_ext, a_k_ext;
+  const T* b; int64_t ldb, b_mn_ext, b_k_ext;
+  int64_t k_len;
+  float* c; int64_t ldc, m, n;
+  int accumulate;
+  int64_t m_tiles;        // set by the launcher
+};
+
+template <typename T> hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st);
+template <typename T> hipError_t launch_strip_grad(StripArgs<T> a, hipStream_t st);
+template <typename T>
+hipError_t launch_dh(const T* g_strip, int64_t ldg, const T* w_strip, int64_t v_len, int64_t n_tok,
+                     int64_t h, float* d_hidden, int accumulate, hipStream_t st);
+template <typename T>
+hipError_t launch_dw(const T* g_strip, int64_t ldg, const T* hidden, int64_t v_len, int64_t n_tok,
+                     int64_t h, float* d_weight_strip, hipStream_t st);
+
+hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st);
+hipError_t launch_fold(const float2* partials, int64_t n_blocks, float* m, float* s, int64_t n,
+                       hipStream_t st);
+hipError_t launch_finalize(const float* m, const float* s, const float* zt, const int32_t* targets,
+                           int64_t n, int32_t ignore_index, int reduction, float* lse,
+                           float* row_loss, float* loss, hipStream_t st);
+hipError_t launch_grad_scale(const int32_t* targets, int64_t n, int32_t ignore_index,
+                             int reduction, const float* grad_out, Control* ctrl, hipStream_t st);
+
+}  // namespace lce

@@ -1,0 +1,395 @@
+// lce_kernels.hip - gfx950 kernels of the strip-wise linear cross-entropy.
+//
+// Forward, per vocabulary strip W_s = W[v0 : v0 + v_len]:
+//   strip_lse   Z^T = W_s . h^T on MFMA; the epilogue reduces each token's
+//               column of the 256 x 256 tile to a partial (max, sum of exp)
+//               per 128 vocabulary rows and captures the target logit.  The
+//               logits never leave registers.
+//   fold        merges the partials of the strip into the running per-token
+//               (max, sum) - the state fold of Ring-DTP (second page, 3.2).
+// and once per pass: state_init before the first strip, finalize after the
+// last (lse = max + log(sum), row loss = lse - target logit, reduction).
+//
+// Backward, per strip: strip_grad recomputes Z^T and writes
+// G = scale * (softmax - onehot) as the input element type into the strip
+// buffer [N, ldG]; gemm_dh forms dH (+)= G . W_s and gemm_dw forms
+// dW_s = G^T . h, both accumulating in fp32.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "lce_kernels.h"
+#include "tile_engine.h"
+
+namespace lce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Tile coordinates of this block: tiles are numbered M-fastest.
+__device__ __forceinline__ void tile_coords(int64_t m_tiles, int64_t* m0, int64_t* n0) {
+  const int64_t b = blockIdx.x;
+  *m0 = (b % m_tiles) * kTile;
+  *n0 = (b / m_tiles) * kTile;
+}
+
+// ---------------------------------------------------------------------------
+// Forward strip: MFMA M = vocabulary rows of the strip, N = tokens, K = H.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int64_t m0, n0;
+  tile_coords(a.m_tiles, &m0, &n0);
+  Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
+  Operand<T> B{a.hidden, a.H, a.N, a.H};
+  Acc acc;
+  tile_mainloop<T, true, true>(A, B, m0, n0, a.H, lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t vrow0 = m0 + wm * kWaveTile;          // first strip row of this wave
+  const int64_t rows_left = a.v_len - vrow0;
+  if (rows_left <= 0) return;                          // wave-uniform
+  const int nrows = rows_left < kWaveTile ? (int)rows_left : kWaveTile;
+  const bool full = nrows == kWaveTile;
+  const int64_t blk = vrow0 / kWaveTile;
+  const int half = lane >> 5;
+
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
+    const bool tok_ok = tok < a.N;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float z = acc.c[mi][ni][e];
+        if (full || acc_row(mi, e, lane) < nrows) mx = fmaxf(mx, z);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mscaled = mx * kLog2e;
+    float sum = 0.f;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, -mscaled));
+        if (full || acc_row(mi, e, lane) < nrows) sum += p;
+      }
+    sum += __shfl_xor(sum, 32);
+    if (half == 0 && tok_ok) a.partials[blk * a.N + tok] = float2{mx, sum};
+
+    // Target logit: at most one (row, token) pair of the whole strip matches.
+    const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
+    const int64_t local = (int64_t)t - (a.v_begin + vrow0);
+    const bool hit = t != a.ignore_index && local >= 0 && local < nrows;
+    if (__any(hit)) {
+      const int lr = (int)local;
+      float zt = 0.f;
+      bool mine = false;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const bool eq = hit && acc_row(mi, e, lane) == lr;
+          zt = eq ? acc.c[mi][ni][e] : zt;
+          mine = mine || eq;
+        }
+      if (mine) a.z_target[tok] = zt;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward strip: same tile, epilogue writes G[tok, v] = scale*(p - onehot).
+// ---------------------------------------------------------------------------
+template <typename T> struct GPack;
+template <> struct GPack<__bf16> {
+  __device__ __forceinline__ static void store(__bf16* dst, float a, float b, float c, float d) {
+    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+    bf16x4_t v{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+    *reinterpret_cast<bf16x4_t*>(dst) = v;
+  }
+};
+template <> struct GPack<float> {
+  __device__ __forceinline__ static void store(float* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{a, b, c, d};
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int64_t m0, n0;
+  tile_coords(a.m_tiles, &m0, &n0);
+  Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
+  Operand<T> B{a.hidden, a.H, a.N, a.H};
+  Acc acc;
+  tile_mainloop<T, true, true>(A, B, m0, n0, a.H, lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t vrow0 = m0 + wm * kWaveTile;
+  const float scale_all = a.ctrl->grad_scale;
+
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
+    if (tok >= a.N) continue;
+    const int32_t t = a.targets[tok];
+    const float sc = t != a.ignore_index ? scale_all : 0.f;
+    const float lse2 = a.lse[tok] * kLog2e;
+    const int64_t tl = (int64_t)t - (a.v_begin + vrow0);  // target row within this wave
+    T* grow = a.g_strip + tok * a.ldg + vrow0;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float g[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = acc_row(mi, 4 * q + i, lane);
+          float p = sc * fast_exp2(__builtin_fmaf(acc.c[mi][ni][4 * q + i], kLog2e, -lse2));
+          p = (vrow0 + r < a.v_len) ? p : 0.f;
+          g[i] = (r == tl) ? p - sc : p;
+        }
+        GPack<T>::store(grow + acc_row(mi, 4 * q, lane), g[0], g[1], g[2], g[3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Plain fp32-output GEMM tile: C[m, n] (+)= sum_k A[m, k] B[n, k].
+// ---------------------------------------------------------------------------
+template <typename T, bool AK, bool BK>
+__global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int64_t m0, n0;
+  tile_coords(g.m_tiles, &m0, &n0);
+  Operand<T> A{g.a, g.lda, g.a_mn_ext, g.a_k_ext};
+  Operand<T> B{g.b, g.ldb, g.b_mn_ext, g.b_k_ext};
+  Acc acc;
+  tile_mainloop<T, AK, BK>(A, B, m0, n0, g.k_len, lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t col = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * kWaveTile + acc_row(mi, e, lane);
+        if (row < g.m && col < g.n) {
+          float* p = g.c + row * g.ldc + col;
+          *p = g.accumulate ? *p + acc.c[mi][ni][e] : acc.c[mi][ni][e];
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small per-token kernels.
+// ---------------------------------------------------------------------------
+__global__ void state_init_kernel(float* m, float* s, float* zt, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    m[i] = -INFINITY;
+    s[i] = 0.f;
+    zt[i] = __builtin_nanf("");
+  }
+}
+
+// Merge (m, s) with (mp, sp): both describe sum_v exp(z_v) as s * e^m.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float mp, float sp) {
+  const float mn = fmaxf(m, mp);
+  if (mn == -INFINITY) return;  // nothing seen on either side
+  s = s * fast_exp2((m - mn) * kLog2e) + sp * fast_exp2((mp - mn) * kLog2e);
+  m = mn;
+}
+
+__global__ void fold_kernel(const float2* __restrict__ partials, int64_t n_blocks, float* m,
+                            float* s, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float mm = m[i], ss = s[i];
+  for (int64_t b = 0; b < n_blocks; ++b) {
+    const float2 p = partials[b * n + i];
+    lse_merge(mm, ss, p.x, p.y);
+  }
+  m[i] = mm;
+  s[i] = ss;
+}
+
+constexpr int kReduceThreads = 1024;
+
+// One block: lse, row loss, n_valid and the reduced loss (fixed-order sums).
+__global__ __launch_bounds__(kReduceThreads) void finalize_kernel(
+    const float* __restrict__ m, const float* __restrict__ s, const float* __restrict__ zt,
+    const int32_t* __restrict__ targets, int64_t n, int32_t ignore_index, int reduction,
+    float* lse, float* row_loss, float* loss) {
+  __shared__ double part_sum[kReduceThreads];
+  __shared__ long long part_cnt[kReduceThreads];
+  double acc = 0.0;
+  long long cnt = 0;
+  for (int64_t i = threadIdx.x; i < n; i += kReduceThreads) {
+    const float l = m[i] + logf(s[i]);
+    lse[i] = l;
+    const bool valid = targets[i] != ignore_index;
+    const float rl = valid ? l - zt[i] : 0.f;
+    if (row_loss) row_loss[i] = rl;
+    acc += (double)rl;
+    cnt += valid ? 1 : 0;
+  }
+  part_sum[threadIdx.x] = acc;
+  part_cnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int w = kReduceThreads / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      part_sum[threadIdx.x] += part_sum[threadIdx.x + w];
+      part_cnt[threadIdx.x] += part_cnt[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double tot = part_sum[0];
+    const long long nv = part_cnt[0];
+    loss[0] = reduction == 0 ? (float)(tot / (double)nv) : (float)tot;
+  }
+}
+
+// One block: count non-ignored rows and form the gradient scale.
+__global__ __launch_bounds__(kReduceThreads) void grad_scale_kernel(
+    const int32_t* __restrict__ targets, int64_t n, int32_t ignore_index, int reduction,
+    const float* __restrict__ grad_out, Control* ctrl) {
+  __shared__ long long part_cnt[kReduceThreads];
+  long long cnt = 0;
+  for (int64_t i = threadIdx.x; i < n; i += kReduceThreads) cnt += targets[i] != ignore_index;
+  part_cnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int w = kReduceThreads / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part_cnt[threadIdx.x] += part_cnt[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const long long nv = part_cnt[0];
+    const float go = grad_out[0];
+    ctrl->n_valid = nv;
+    ctrl->grad_scale = reduction == 0 ? (nv > 0 ? (float)((double)go / (double)nv) : 0.f) : go;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <typename T>
+static hipError_t set_lds(const void* fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+}
+
+template <typename T>
+hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st) {
+  a.m_tiles = cdiv(a.v_len, kTile);
+  const int64_t blocks = a.m_tiles * cdiv(a.N, kTile);
+  hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_lse_kernel<T>));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(strip_lse_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, st, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_strip_grad(StripArgs<T> a, hipStream_t st) {
+  a.m_tiles = cdiv(a.v_len, kTile);
+  const int64_t blocks = a.m_tiles * cdiv(a.N, kTile);
+  hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_grad_kernel<T>));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(strip_grad_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, bool AK, bool BK>
+static hipError_t launch_gemm(GemmArgs<T> g, hipStream_t st) {
+  g.m_tiles = cdiv(g.m, kTile);
+  const int64_t blocks = g.m_tiles * cdiv(g.n, kTile);
+  hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&gemm_f32out_kernel<T, AK, BK>));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_f32out_kernel<T, AK, BK>), dim3((unsigned)blocks), dim3(kThreads),
+                     kLdsBytes, st, g);
+  return hipGetLastError();
+}
+
+// dH[N, H] (+)= G[N, :v_len] . W_s[v_len, H]: M = tokens, N = H, K = strip rows.
+template <typename T>
+hipError_t launch_dh(const T* g_strip, int64_t ldg, const T* w_strip, int64_t v_len, int64_t n_tok,
+                     int64_t h, float* d_hidden, int accumulate, hipStream_t st) {
+  GemmArgs<T> g{};
+  g.a = g_strip; g.lda = ldg; g.a_mn_ext = n_tok; g.a_k_ext = v_len;   // K-contiguous
+  g.b = w_strip; g.ldb = h;   g.b_mn_ext = h;     g.b_k_ext = v_len;   // MN-contiguous
+  g.k_len = v_len;
+  g.c = d_hidden; g.ldc = h; g.m = n_tok; g.n = h; g.accumulate = accumulate;
+  return launch_gemm<T, true, false>(g, st);
+}
+
+// dW_s[v_len, H] = G[:, :v_len]^T . h: M = strip rows, N = H, K = tokens.
+template <typename T>
+hipError_t launch_dw(const T* g_strip, int64_t ldg, const T* hidden, int64_t v_len, int64_t n_tok,
+                     int64_t h, float* d_weight_strip, hipStream_t st) {
+  GemmArgs<T> g{};
+  const int64_t cols = cdiv(v_len, 8) * 8;  // chunk-aligned; the pad columns of G are zero
+  g.a = g_strip; g.lda = ldg; g.a_mn_ext = cols; g.a_k_ext = n_tok;    // MN-contiguous
+  g.b = hidden;  g.ldb = h;   g.b_mn_ext = h;    g.b_k_ext = n_tok;    // MN-contiguous
+  g.k_len = n_tok;
+  g.c = d_weight_strip; g.ldc = h; g.m = v_len; g.n = h; g.accumulate = 0;
+  return launch_gemm<T, false, false>(g, st);
+}
+
+hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(state_init_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, m, s, zt, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold(const float2* partials, int64_t n_blocks, float* m, float* s, int64_t n,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, partials,
+                     n_blocks, m, s, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* m, const float* s, const float* zt, const int32_t* targets,
+                           int64_t n, int32_t ignore_index, int reduction, float* lse,
+                           float* row_loss, float* loss, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kReduceThreads), 0, st, m, s, zt, targets, n,
+                     ignore_index, reduction, lse, row_loss, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_scale(const int32_t* targets, int64_t n, int32_t ignore_index,
+                             int reduction, const float* grad_out, Control* ctrl, hipStream_t st) {
+  hipLaunchKernelGGL(grad_scale_kernel, dim3(1), dim3(kReduceThreads), 0, st, targets, n,
+                     ignore_index, reduction, grad_out, ctrl);
+  return hipGetLastError();
+}
+
+template hipError_t launch_strip_lse<__bf16>(StripArgs<__bf16>, hipStream_t);
+template hipError_t launch_strip_lse<float>(StripArgs<float>, hipStream_t);
+template hipError_t launch_strip_grad<__bf16>(StripArgs<__bf16>, hipStream_t);
+template hipError_t launch_strip_grad<float>(StripArgs<float>, hipStream_t);
+template hipError_t launch_dh<__bf16>(const __bf16*, int64_t, const __bf16*, int64_t, int64_t,
+                                      int64_t, float*, int, hipStream_t);
+template hipError_t launch_dh<float>(const float*, int64_t, const float*, int64_t, int64_t,
+                                     int64_t, float*, int, hipStream_t);
+template hipError_t launch_dw<__bf16>(const __bf16*, int64_t, const __bf16*, int64_t, int64_t,
+                                      int64_t, float*, hipStream_t);
+template hipError_t launch_dw<float>(const float*, int64_t, const float*, int64_t, int64_t,
+                                     int64_t, float*, hipStream_t);
+
+}  // namespace lce
