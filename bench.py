@@ -1,0 +1,264 @@
+"""Benchmark of the strip-wise linear cross-entropy on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is the whole path on one batch: lce_forward (every strip folded into
+the running per-token state, then finalised) and lce_backward (every strip
+recomputed, its gradient strip formed, dH and dW accumulated), with inputs
+already resident in HBM.  The metric is the fused fwd+bwd rate 8*N*H*V / time
+in TFLOP/s, on the 131072-token workload (H=2048, V=151936, strip 8192, bf16)
+unless --workload says otherwise.
+
+Printed on one JSON line: the metric, the per-kernel roofline of the kernel
+that takes most of the time (its algorithmic FLOP per launch over its
+average launch time, measured with HIP events on the library's stream), and
+the CPU oracle timed on a bounded sample of the same workload on the host
+cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused linear-CE fwd+bwd TFLOP/s (8·N·H·V) and % bf16 MFMA peak"
+DEFAULT_WORKLOAD = "bf16_n128k_h2k_v152k"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X published dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-kernel timing pass")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (HBM counter scale)")
+    return ap.parse_args()
+
+
+def ensure_built():
+    from vocab_projection_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from vocab_projection_amd import build
+        build.build()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    ensure_built()
+    import torch
+    from vocab_projection_amd import binding as B
+    from vocab_projection_amd import synthetic as S
+
+    w = S.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    t0 = time.time()
+    hid_np = S.hidden(w, threads=16)
+    w_np = S.weight(w, threads=16)
+    t_np = S.targets(w)
+    h = torch.from_numpy(hid_np).to(dev).to(dt)
+    W = torch.from_numpy(w_np).to(dev).to(dt)
+    t = torch.from_numpy(t_np).to(dev)
+    log(f"inputs {w.name}: {time.time() - t0:.1f}s")
+
+    p = B.make_problem(h, W, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, strip=w.strip)
+    ws = B.workspace(p, dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.n_tokens, dtype=torch.float32, device=dev)
+    dh = torch.empty(h.shape, dtype=torch.float32, device=dev)
+    dw = torch.empty(W.shape, dtype=torch.float32, device=dev)
+    go = torch.tensor([w.grad_out], dtype=torch.float32, device=dev)
+    order = S.fold_order(w)
+    natural = w.shards == 0
+
+    def step():
+        if natural:
+            B.lce_forward(p, h, W, t, loss, lse, None, ws)
+            B.lce_backward(p, h, W, t, lse, go, dh, dw, ws)
+        else:
+            B.lce_forward_begin(p, ws)
+            for v0, vl in order:
+                B.lce_forward_fold(p, h, W[v0:v0 + vl], v0, vl, t, ws)
+            B.lce_forward_end(p, t, loss, lse, None, ws)
+            B.lce_backward_begin(p, t, go, ws)
+            for k, (v0, vl) in enumerate(order):
+                B.lce_backward_fold(p, h, W[v0:v0 + vl], v0, vl, t, lse, dh, k > 0,
+                                    dw[v0:v0 + vl], ws)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} loss={loss.item():.6f}")
+
+    # memory: nothing beyond the caller's buffers may be allocated by a step
+    free_before = torch.cuda.mem_get_info(dev)[0]
+    torch.cuda.reset_peak_memory_stats(dev)
+    alloc_before = torch.cuda.memory_allocated(dev)
+
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step (wall {wall:.2f}s)")
+    peak_alloc_extra = torch.cuda.max_memory_allocated(dev) - alloc_before
+    free_after = torch.cuda.mem_get_info(dev)[0]
+
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_tokens": w.n_tokens, "hidden": w.hidden,
+                   "vocab": w.vocab, "strip": w.strip, "reduction": w.reduction,
+                   "fold_order": "natural" if natural else f"ring of {w.shards} shards"},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "memory": {
+            "workspace_bytes": B.lce_workspace_bytes(p),
+            "strip_bytes": w.n_tokens * w.strip * w.elt_bytes,
+            "full_logits_bytes": w.n_tokens * w.vocab * w.elt_bytes,
+            "allocator_peak_extra_bytes": int(peak_alloc_extra),
+            "device_free_delta_bytes": int(free_before - free_after),
+        },
+    }
+
+    if not args.no_breakdown:
+        result["kernels"], result["roofline"] = kernel_breakdown(
+            args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, loss, peak)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, hid_np, w_np, t_np, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, loss, peak):
+    """Run the same steps through the step-level calls with an event pair around
+    every kernel launch of the fold loops; return per-kernel times and the
+    roofline of the kernel with the largest total time."""
+    kernels = {
+        "strip_lse": ("lce::strip_lse_kernel", "fwd", B.LCE_STEP_STRIP),
+        "merge": ("lce::fold_kernel", "fwd", B.LCE_STEP_MERGE),
+        "strip_grad": ("lce::strip_grad_kernel", "bwd", B.LCE_STEP_GRAD),
+        "gemm_dh": ("lce::gemm_f32out_kernel<A K-contig, B MN-contig>", "bwd", B.LCE_STEP_DHIDDEN),
+        "gemm_dw": ("lce::gemm_f32out_kernel<A MN-contig, B MN-contig>", "bwd", B.LCE_STEP_DWEIGHT),
+    }
+    flops_per_row = {"strip_lse": 2.0, "strip_grad": 2.0, "gemm_dh": 2.0, "gemm_dw": 2.0}
+    recs = {k: [] for k in kernels}
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    for _ in range(args.steps):
+        B.lce_forward_begin(p, ws)
+        for v0, vl in order:
+            for k in ("strip_lse", "merge"):
+                a = ev()
+                B.lce_forward_fold_steps(p, h, W[v0:v0 + vl], v0, vl, t, ws, kernels[k][2])
+                recs[k].append((a, ev(), vl))
+        B.lce_forward_end(p, t, loss, lse, None, ws)
+        B.lce_backward_begin(p, t, go, ws)
+        for i, (v0, vl) in enumerate(order):
+            for k in ("strip_grad", "gemm_dh", "gemm_dw"):
+                a = ev()
+                B.lce_backward_fold_steps(p, h, W[v0:v0 + vl], v0, vl, t, lse, dh, i > 0,
+                                          dw[v0:v0 + vl], ws, kernels[k][2])
+                recs[k].append((a, ev(), vl))
+    torch.cuda.synchronize()
+    out = {}
+    for k, lst in recs.items():
+        ms = [a.elapsed_time(b) for a, b, _ in lst]
+        entry = {"kernel": kernels[k][0], "launches": len(ms), "avg_ms": round(float(np.mean(ms)), 4),
+                 "total_ms_per_step": round(float(np.sum(ms)) / args.steps, 3)}
+        if k in flops_per_row:
+            fl = sum(flops_per_row[k] * w.n_tokens * w.hidden * vl for _, _, vl in lst)
+            entry["tflops"] = round(fl / (np.sum(ms) * 1e-3) / 1e12, 2)
+            entry["algorithmic_flop_per_launch"] = fl / len(ms)
+        out[k] = entry
+    dom = max(flops_per_row, key=lambda k: out[k]["total_ms_per_step"])
+    achieved = out[dom]["tflops"]
+    roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None, "kernel": out[dom]["kernel"],
+            "step": dom, "avg_launch_ms": out[dom]["avg_ms"],
+            "algorithmic_flop_per_launch": out[dom]["algorithmic_flop_per_launch"]}
+    log("per-kernel:", json.dumps(out))
+    return out, roof
+
+
+def cpu_baseline(w, hid_np, wt, t_np, rows):
+    """The CPU oracle, as it is, on the first `rows` tokens with the full weight."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import lce_oracle as O
+    from vocab_projection_amd import synthetic as S
+
+    hs, ts = hid_np[:rows], t_np[:rows]
+    t0 = time.perf_counter()
+    O.forward(hs, wt, ts, ignore_index=S.IGNORE_INDEX, reduction=w.reduction)
+    O.backward(hs, wt, ts, ignore_index=S.IGNORE_INDEX, reduction=w.reduction,
+               grad_out=w.grad_out)
+    sec = time.perf_counter() - t0
+    flops = 8.0 * rows * w.hidden * w.vocab
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(flops / sec / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(sec, 2),
+            "sample": f"first {rows} of {w.n_tokens} tokens with the full weight "
+                      f"(H={w.hidden}, V={w.vocab}): oracle forward + backward in float64, "
+                      f"8*{rows}*H*V FLOP"}
+
+
+if __name__ == "__main__":
+    main()

@@ -147,6 +147,39 @@ lce_status_t lce_backward_fold(const lce_problem_t* p, const void* hidden,
                                int accumulate, float* d_weight_strip, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* ---- The steps of one fold, one kernel each ----
+ * lce_forward_fold and lce_backward_fold run every step of their fold in
+ * order; the calls below run only the steps named in `steps` (a bit set of
+ * lce_step_t), so that a caller can time each kernel on its stream, as the
+ * first page's paired test does for time next to loss, gradient and peak
+ * (section 8, "Paired Testing").  Running the steps of a fold in order in
+ * separate calls is the same computation as one fold call.
+ *   forward:  LCE_STEP_STRIP - logits of the strip and their per-token
+ *             (max, sum of exp) partials plus the target logit, in registers;
+ *             LCE_STEP_MERGE - fold the partials into the running state.
+ *   backward: LCE_STEP_GRAD - recompute the strip and write its G;
+ *             LCE_STEP_DHIDDEN - d_hidden (+)= G . W_strip;
+ *             LCE_STEP_DWEIGHT - d_weight_strip = G^T . h. */
+typedef enum lce_step {
+  LCE_STEP_STRIP = 1,
+  LCE_STEP_MERGE = 2,
+  LCE_STEP_GRAD = 1,
+  LCE_STEP_DHIDDEN = 2,
+  LCE_STEP_DWEIGHT = 4,
+  LCE_STEP_ALL = 7
+} lce_step_t;
+
+lce_status_t lce_forward_fold_steps(const lce_problem_t* p, const void* hidden,
+                                    const void* weight_strip, int64_t v_begin, int64_t v_len,
+                                    const int32_t* targets, void* workspace,
+                                    size_t workspace_bytes, unsigned steps, hipStream_t stream);
+
+lce_status_t lce_backward_fold_steps(const lce_problem_t* p, const void* hidden,
+                                     const void* weight_strip, int64_t v_begin, int64_t v_len,
+                                     const int32_t* targets, const float* lse, float* d_hidden,
+                                     int accumulate, float* d_weight_strip, void* workspace,
+                                     size_t workspace_bytes, unsigned steps, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

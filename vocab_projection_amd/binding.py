@@ -51,6 +51,10 @@ _SIGNATURES = {
     "lce_backward_begin": (ctypes.c_int, [_P, _VP, _VP, _VP, _SZ, _VP]),
     "lce_backward_fold": (ctypes.c_int, [_P, _VP, _VP, _I64, _I64, _VP, _VP, _VP, ctypes.c_int,
                                          _VP, _VP, _SZ, _VP]),
+    "lce_forward_fold_steps": (ctypes.c_int, [_P, _VP, _VP, _I64, _I64, _VP, _VP, _SZ,
+                                              ctypes.c_uint, _VP]),
+    "lce_backward_fold_steps": (ctypes.c_int, [_P, _VP, _VP, _I64, _I64, _VP, _VP, _VP,
+                                               ctypes.c_int, _VP, _VP, _SZ, ctypes.c_uint, _VP]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -152,6 +156,26 @@ def lce_backward_fold(p, hidden, weight_strip, v_begin, v_len, targets, lse, d_h
                                     v_len, _ptr(targets), _ptr(lse), _ptr(d_hidden),
                                     int(bool(accumulate)), _ptr(d_weight_strip),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def lce_forward_fold_steps(p, hidden, weight_strip, v_begin, v_len, targets, workspace, steps,
+                           stream=None):
+    _check(load().lce_forward_fold_steps(ctypes.byref(p), _ptr(hidden), _ptr(weight_strip),
+                                         v_begin, v_len, _ptr(targets), _ptr(workspace),
+                                         workspace.numel(), steps, _stream(stream)))
+
+
+def lce_backward_fold_steps(p, hidden, weight_strip, v_begin, v_len, targets, lse, d_hidden,
+                            accumulate, d_weight_strip, workspace, steps, stream=None):
+    _check(load().lce_backward_fold_steps(ctypes.byref(p), _ptr(hidden), _ptr(weight_strip),
+                                          v_begin, v_len, _ptr(targets), _ptr(lse),
+                                          _ptr(d_hidden), int(bool(accumulate)),
+                                          _ptr(d_weight_strip), _ptr(workspace),
+                                          workspace.numel(), steps, _stream(stream)))
+
+
+LCE_STEP_STRIP, LCE_STEP_MERGE = 1, 2
+LCE_STEP_GRAD, LCE_STEP_DHIDDEN, LCE_STEP_DWEIGHT, LCE_STEP_ALL = 1, 2, 4, 7
 
 
 # ---- torch-facing helpers ----

@@ -123,7 +123,7 @@ lce_status_t check_strip(const Plan& pl, const void* weight_strip, int64_t v_beg
 template <typename T>
 lce_status_t fold_fwd(const Plan& pl, const void* hidden, const void* weight_strip,
                       int64_t v_begin, int64_t v_len, const int32_t* targets, void* ws,
-                      hipStream_t st) {
+                      unsigned steps, hipStream_t st) {
   Carve c = carve(pl, ws);
   lce::StripArgs<T> a{};
   a.hidden = static_cast<const T*>(hidden);
@@ -136,17 +136,22 @@ lce_status_t fold_fwd(const Plan& pl, const void* hidden, const void* weight_str
   a.ignore_index = pl.ignore_index;
   a.partials = reinterpret_cast<float2*>(c.strip);
   a.z_target = c.zt;
-  lce_status_t s = launched(lce::launch_strip_lse<T>(a, st));
-  if (s != LCE_OK) return s;
-  const int64_t nblk = (v_len + kPartRows - 1) / kPartRows;
-  return launched(lce::launch_fold(a.partials, nblk, c.m, c.s, pl.N, st));
+  if (steps & LCE_STEP_STRIP) {
+    lce_status_t s = launched(lce::launch_strip_lse<T>(a, st));
+    if (s != LCE_OK) return s;
+  }
+  if (steps & LCE_STEP_MERGE) {
+    const int64_t nblk = (v_len + kPartRows - 1) / kPartRows;
+    return launched(lce::launch_fold(a.partials, nblk, c.m, c.s, pl.N, st));
+  }
+  return LCE_OK;
 }
 
 template <typename T>
 lce_status_t fold_bwd(const Plan& pl, const void* hidden, const void* weight_strip,
                       int64_t v_begin, int64_t v_len, const int32_t* targets, const float* lse,
                       float* d_hidden, int accumulate, float* d_weight_strip, void* ws,
-                      hipStream_t st) {
+                      unsigned steps, hipStream_t st) {
   Carve c = carve(pl, ws);
   lce::StripArgs<T> a{};
   a.hidden = static_cast<const T*>(hidden);
@@ -161,13 +166,20 @@ lce_status_t fold_bwd(const Plan& pl, const void* hidden, const void* weight_str
   a.ctrl = c.ctrl;
   a.g_strip = reinterpret_cast<T*>(c.strip);
   a.ldg = pl.ldg;
-  lce_status_t s = launched(lce::launch_strip_grad<T>(a, st));
-  if (s != LCE_OK) return s;
-  s = launched(lce::launch_dh<T>(a.g_strip, pl.ldg, a.weight_strip, v_len, pl.N, pl.H, d_hidden,
-                                 accumulate, st));
-  if (s != LCE_OK) return s;
-  return launched(lce::launch_dw<T>(a.g_strip, pl.ldg, a.hidden, v_len, pl.N, pl.H,
-                                    d_weight_strip, st));
+  lce_status_t s = LCE_OK;
+  if (steps & LCE_STEP_GRAD) {
+    if ((s = launched(lce::launch_strip_grad<T>(a, st))) != LCE_OK) return s;
+  }
+  if (steps & LCE_STEP_DHIDDEN) {
+    s = launched(lce::launch_dh<T>(a.g_strip, pl.ldg, a.weight_strip, v_len, pl.N, pl.H, d_hidden,
+                                   accumulate, st));
+    if (s != LCE_OK) return s;
+  }
+  if (steps & LCE_STEP_DWEIGHT) {
+    s = launched(lce::launch_dw<T>(a.g_strip, pl.ldg, a.hidden, v_len, pl.N, pl.H,
+                                   d_weight_strip, st));
+  }
+  return s;
 }
 
 }  // namespace
@@ -210,15 +222,26 @@ lce_status_t lce_forward_fold(const lce_problem_t* p, const void* hidden,
                               const void* weight_strip, int64_t v_begin, int64_t v_len,
                               const int32_t* targets, void* ws, size_t ws_bytes,
                               hipStream_t stream) {
+  return lce_forward_fold_steps(p, hidden, weight_strip, v_begin, v_len, targets, ws, ws_bytes,
+                                LCE_STEP_STRIP | LCE_STEP_MERGE, stream);
+}
+
+lce_status_t lce_forward_fold_steps(const lce_problem_t* p, const void* hidden,
+                                    const void* weight_strip, int64_t v_begin, int64_t v_len,
+                                    const int32_t* targets, void* ws, size_t ws_bytes,
+                                    unsigned steps, hipStream_t stream) {
   Plan pl;
   lce_status_t s = make_plan(p, &pl);
   if (s != LCE_OK) return s;
   if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
   if (!hidden || !aligned(hidden) || !targets) return LCE_ERR_INVALID_VALUE;
   if ((s = check_strip(pl, weight_strip, v_begin, v_len)) != LCE_OK) return s;
+  if (steps & ~(unsigned)(LCE_STEP_STRIP | LCE_STEP_MERGE)) return LCE_ERR_INVALID_VALUE;
   return pl.dtype == LCE_BF16
-             ? fold_fwd<__bf16>(pl, hidden, weight_strip, v_begin, v_len, targets, ws, stream)
-             : fold_fwd<float>(pl, hidden, weight_strip, v_begin, v_len, targets, ws, stream);
+             ? fold_fwd<__bf16>(pl, hidden, weight_strip, v_begin, v_len, targets, ws, steps,
+                                stream)
+             : fold_fwd<float>(pl, hidden, weight_strip, v_begin, v_len, targets, ws, steps,
+                               stream);
 }
 
 lce_status_t lce_forward_end(const lce_problem_t* p, const int32_t* targets, float* loss,
@@ -272,6 +295,15 @@ lce_status_t lce_backward_fold(const lce_problem_t* p, const void* hidden,
                                const int32_t* targets, const float* lse, float* d_hidden,
                                int accumulate, float* d_weight_strip, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
+  return lce_backward_fold_steps(p, hidden, weight_strip, v_begin, v_len, targets, lse, d_hidden,
+                                 accumulate, d_weight_strip, ws, ws_bytes, LCE_STEP_ALL, stream);
+}
+
+lce_status_t lce_backward_fold_steps(const lce_problem_t* p, const void* hidden,
+                                     const void* weight_strip, int64_t v_begin, int64_t v_len,
+                                     const int32_t* targets, const float* lse, float* d_hidden,
+                                     int accumulate, float* d_weight_strip, void* ws,
+                                     size_t ws_bytes, unsigned steps, hipStream_t stream) {
   Plan pl;
   lce_status_t s = make_plan(p, &pl);
   if (s != LCE_OK) return s;
@@ -280,11 +312,12 @@ lce_status_t lce_backward_fold(const lce_problem_t* p, const void* hidden,
     return LCE_ERR_INVALID_VALUE;
   if (!aligned(d_hidden) || !aligned(d_weight_strip)) return LCE_ERR_INVALID_VALUE;
   if ((s = check_strip(pl, weight_strip, v_begin, v_len)) != LCE_OK) return s;
+  if (steps & ~(unsigned)LCE_STEP_ALL) return LCE_ERR_INVALID_VALUE;
   return pl.dtype == LCE_BF16
              ? fold_bwd<__bf16>(pl, hidden, weight_strip, v_begin, v_len, targets, lse, d_hidden,
-                                accumulate, d_weight_strip, ws, stream)
+                                accumulate, d_weight_strip, ws, steps, stream)
              : fold_bwd<float>(pl, hidden, weight_strip, v_begin, v_len, targets, lse, d_hidden,
-                               accumulate, d_weight_strip, ws, stream);
+                               accumulate, d_weight_strip, ws, steps, stream);
 }
 
 lce_status_t lce_backward(const lce_problem_t* p, const void* hidden, const void* weight,
