@@ -22,7 +22,7 @@ struct StripArgs {
   int64_t N, H;
   int64_t v_begin, v_len;
   int32_t ignore_index;
-  int64_t m_tiles;        // set by the launcher
+  int64_t m_tiles, n_tiles, group_m;  // tile order, set by the launcher
   // forward
   float2* partials;       // [ceil(v_len / 128), N]
   float* z_target;        // [N]
@@ -40,7 +40,7 @@ struct GemmArgs {
   int64_t k_len;
   float* c; int64_t ldc, m, n;
   int accumulate;
-  int64_t m_tiles;        // set by the launcher
+  int64_t m_tiles, n_tiles, group_m;  // tile order, set by the launcher
 };
 
 template <typename T> hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st);

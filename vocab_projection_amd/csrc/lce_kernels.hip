@@ -27,11 +27,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Tile coordinates of this block: tiles are numbered M-fastest.
-__device__ __forceinline__ void tile_coords(int64_t m_tiles, int64_t* m0, int64_t* n0) {
+constexpr int kXcds = 8;  // blocks are dispatched to the 8 XCDs round-robin
+
+// Tile coordinates of this block.  Tiles are ordered in groups of group_m
+// M-tiles: within a group N advances after every group_m tiles, so that
+// consecutive tiles share operand rows.  Each XCD (block b runs on XCD b % 8)
+// is given one contiguous range of that order, so the blocks resident on one
+// XCD at the same time work on neighbouring tiles and share its L2.
+__device__ __forceinline__ void tile_coords(int64_t m_tiles, int64_t n_tiles, int64_t group_m,
+                                            int64_t* m0, int64_t* n0) {
+  const int64_t total = m_tiles * n_tiles;
   const int64_t b = blockIdx.x;
-  *m0 = (b % m_tiles) * kTile;
-  *n0 = (b / m_tiles) * kTile;
+  const int64_t x = b % kXcds, j = b / kXcds;
+  const int64_t q = total / kXcds, r = total % kXcds;
+  const int64_t t = x * q + (x < r ? x : r) + j;  // a bijection of [0, total)
+  const int64_t per_group = group_m * n_tiles;
+  const int64_t g = t / per_group;
+  const int64_t first_m = g * group_m;
+  const int64_t gm = m_tiles - first_m < group_m ? m_tiles - first_m : group_m;
+  const int64_t local = t - g * per_group;
+  *m0 = (first_m + local % gm) * kTile;
+  *n0 = (local / gm) * kTile;
 }
 
 // ---------------------------------------------------------------------------
@@ -41,7 +57,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t m0, n0;
-  tile_coords(a.m_tiles, &m0, &n0);
+  tile_coords(a.m_tiles, a.n_tiles, a.group_m, &m0, &n0);
   Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
   Operand<T> B{a.hidden, a.H, a.N, a.H};
   Acc acc;
@@ -58,6 +74,18 @@ __global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) 
   const int64_t blk = vrow0 / kWaveTile;
   const int half = lane >> 5;
 
+  if (!full) {
+    // rows past the strip's end: -inf adds nothing to the max or the sum
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool out = acc_row(mi, e, lane) >= nrows;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc.c[mi][ni][e] = out ? -INFINITY : acc.c[mi][ni][e];
+      }
+  }
+
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
@@ -66,20 +94,15 @@ __global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) 
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float z = acc.c[mi][ni][e];
-        if (full || acc_row(mi, e, lane) < nrows) mx = fmaxf(mx, z);
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc.c[mi][ni][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mscaled = mx * kLog2e;
     float sum = 0.f;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, -mscaled));
-        if (full || acc_row(mi, e, lane) < nrows) sum += p;
-      }
+      for (int e = 0; e < 16; ++e)
+        sum += fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, -mscaled));
     sum += __shfl_xor(sum, 32);
     if (half == 0 && tok_ok) a.partials[blk * a.N + tok] = float2{mx, sum};
 
@@ -107,17 +130,25 @@ __global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) 
 // ---------------------------------------------------------------------------
 // Backward strip: same tile, epilogue writes G[tok, v] = scale*(p - onehot).
 // ---------------------------------------------------------------------------
+// Four consecutive gradient values of one token row, stored with one buffer
+// store (8 bytes of bf16 or 16 bytes of f32) at byte offset voff of the row.
 template <typename T> struct GPack;
 template <> struct GPack<__bf16> {
-  __device__ __forceinline__ static void store(__bf16* dst, float a, float b, float c, float d) {
-    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-    bf16x4_t v{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
-    *reinterpret_cast<bf16x4_t*>(dst) = v;
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, float a,
+                                               float b, float c, float d) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t lo{(__bf16)a, (__bf16)b};
+    const bf16x2_t hi{(__bf16)c, (__bf16)d};
+    const u32x2_t v{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
   }
 };
 template <> struct GPack<float> {
-  __device__ __forceinline__ static void store(float* dst, float a, float b, float c, float d) {
-    *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{a, b, c, d};
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, float a,
+                                               float b, float c, float d) {
+    const u32x4_t v{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
   }
 };
 
@@ -125,7 +156,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t m0, n0;
-  tile_coords(a.m_tiles, &m0, &n0);
+  tile_coords(a.m_tiles, a.n_tiles, a.group_m, &m0, &n0);
   Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
   Operand<T> B{a.hidden, a.H, a.N, a.H};
   Acc acc;
@@ -136,16 +167,23 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t vrow0 = m0 + wm * kWaveTile;
   const float scale_all = a.ctrl->grad_scale;
+  // G rows n0.. of the strip buffer, from column m0: byte offset
+  // (tok - n0) * ldg * elt + (col - m0) * elt; rows past N are out of range.
+  const int64_t row_bytes = a.ldg * (int64_t)sizeof(T);
+  const __amdgpu_buffer_rsrc_t gbuf = make_buffer(
+      a.g_strip + n0 * a.ldg + m0, (a.N - n0) * row_bytes - m0 * (int64_t)sizeof(T));
 
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
-    const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
-    if (tok >= a.N) continue;
-    const int32_t t = a.targets[tok];
+    const int tok_local = wn * kWaveTile + ni * 32 + (lane & 31);
+    const int64_t tok = n0 + tok_local;
+    const bool tok_ok = tok < a.N;
+    const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
     const float sc = t != a.ignore_index ? scale_all : 0.f;
-    const float lse2 = a.lse[tok] * kLog2e;
+    const float lse2 = (tok_ok ? a.lse[tok] : 0.f) * kLog2e;
     const int64_t tl = (int64_t)t - (a.v_begin + vrow0);  // target row within this wave
-    T* grow = a.g_strip + tok * a.ldg + vrow0;
+    const uint32_t vbase = (uint32_t)(tok_local * row_bytes) +
+                           (uint32_t)((wm * kWaveTile + (lane >> 5) * 4) * sizeof(T));
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -158,7 +196,8 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
           p = (vrow0 + r < a.v_len) ? p : 0.f;
           g[i] = (r == tl) ? p - sc : p;
         }
-        GPack<T>::store(grow + acc_row(mi, 4 * q, lane), g[0], g[1], g[2], g[3]);
+        GPack<T>::store(gbuf, vbase + (uint32_t)((mi * 32 + q * 8) * sizeof(T)), g[0], g[1], g[2],
+                        g[3]);
       }
   }
 }
@@ -170,7 +209,7 @@ template <typename T, bool AK, bool BK>
 __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t m0, n0;
-  tile_coords(g.m_tiles, &m0, &n0);
+  tile_coords(g.m_tiles, g.n_tiles, g.group_m, &m0, &n0);
   Operand<T> A{g.a, g.lda, g.a_mn_ext, g.a_k_ext};
   Operand<T> B{g.b, g.ldb, g.b_mn_ext, g.b_k_ext};
   Acc acc;
@@ -179,18 +218,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
+  // C from (m0, n0): byte offset (row - m0) * ldc * 4 + (col - n0) * 4.  Rows
+  // past m fall past the record count; columns past n get an out-of-range
+  // offset, since they would otherwise land in the next row.
+  const uint32_t ldc4 = (uint32_t)(g.ldc * 4);
+  const __amdgpu_buffer_rsrc_t cbuf =
+      make_buffer(g.c + m0 * g.ldc + n0, (g.m - m0) * g.ldc * 4 - n0 * 4);
+  uint32_t vcol[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int col = wn * kWaveTile + ni * 32 + (lane & 31);
+    vcol[ni] = n0 + col < g.n ? (uint32_t)((wm * kWaveTile + (lane >> 5) * 4) * ldc4 + col * 4)
+                              : kOutOfRange;
+  }
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int64_t col = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t roff = (uint32_t)(mi * 32 + (e >> 2) * 8 + (e & 3)) * ldc4;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * kWaveTile + acc_row(mi, e, lane);
-        if (row < g.m && col < g.n) {
-          float* p = g.c + row * g.ldc + col;
-          *p = g.accumulate ? *p + acc.c[mi][ni][e] : acc.c[mi][ni][e];
+      for (int ni = 0; ni < 4; ++ni) {
+        const uint32_t off = vcol[ni] + roff;
+        float v = acc.c[mi][ni][e];
+        if (g.accumulate) {
+          v += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cbuf, off, 0, 0));
         }
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), cbuf, off, 0, 0);
       }
     }
 }
@@ -296,10 +349,18 @@ static hipError_t set_lds(const void* fn) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
 }
 
+// M-tiles per group of the tile order: 8 vocabulary tiles of a strip (their
+// W rows stay in L2 while token tiles stream past).
+constexpr int64_t kStripGroupM = 8;
+// Output GEMMs: 4 M-tiles per group, all N-tiles of those rows.
+constexpr int64_t kGemmGroupM = 4;
+
 template <typename T>
 hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st) {
   a.m_tiles = cdiv(a.v_len, kTile);
-  const int64_t blocks = a.m_tiles * cdiv(a.N, kTile);
+  a.n_tiles = cdiv(a.N, kTile);
+  a.group_m = kStripGroupM;
+  const int64_t blocks = a.m_tiles * a.n_tiles;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_lse_kernel<T>));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(strip_lse_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, st, a);
@@ -309,7 +370,9 @@ hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st) {
 template <typename T>
 hipError_t launch_strip_grad(StripArgs<T> a, hipStream_t st) {
   a.m_tiles = cdiv(a.v_len, kTile);
-  const int64_t blocks = a.m_tiles * cdiv(a.N, kTile);
+  a.n_tiles = cdiv(a.N, kTile);
+  a.group_m = kStripGroupM;
+  const int64_t blocks = a.m_tiles * a.n_tiles;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_grad_kernel<T>));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(strip_grad_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, st, a);
@@ -319,7 +382,9 @@ hipError_t launch_strip_grad(StripArgs<T> a, hipStream_t st) {
 template <typename T, bool AK, bool BK>
 static hipError_t launch_gemm(GemmArgs<T> g, hipStream_t st) {
   g.m_tiles = cdiv(g.m, kTile);
-  const int64_t blocks = g.m_tiles * cdiv(g.n, kTile);
+  g.n_tiles = cdiv(g.n, kTile);
+  g.group_m = kGemmGroupM;
+  const int64_t blocks = g.m_tiles * g.n_tiles;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&gemm_f32out_kernel<T, AK, BK>));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gemm_f32out_kernel<T, AK, BK>), dim3((unsigned)blocks), dim3(kThreads),

@@ -1,21 +1,28 @@
 // tile_engine.h - one 256x256 MFMA tile of C = A . B^T on gfx950 (CDNA4).
 //
 // A block of 256 threads (four wave64s in a 2x2 grid, each owning a 128x128
-// sub-tile) walks K in stages of 128 bytes per row: 64 bf16 or 32 f32
-// elements.  Each stage of both operands is staged in LDS (64 KiB), double
-// buffered (128 KiB of the 160 KiB per CU), and read back as 16-byte
-// fragments that feed v_mfma_f32_32x32x16_bf16 (bf16) or four
-// v_mfma_f32_32x32x2f32 (f32), accumulating in fp32.
+// sub-tile of fp32 accumulators) walks K in stages of 128 bytes per row:
+// 64 bf16 or 32 f32 elements, so that every global request is a whole
+// 128-byte line.  Stages are copied from global memory straight into LDS with
+// buffer_load ... lds (no register staging), two stages deep (2 x 64 KiB):
+// the next stage is in flight while one is read.
+// Fragments are read back from LDS as 16-byte K-runs that feed
+// v_mfma_f32_32x32x16_bf16 (bf16) or four v_mfma_f32_32x32x2_f32 (f32).
 //
-// Operands may be stored K-contiguous (element (mn, k) at base[mn*ld + k]) or
-// MN-contiguous (element (mn, k) at base[k*ld + mn]).  Either way the LDS
-// copy is K-contiguous: 256 rows of eight 16-byte chunks, the chunk index
-// XOR-swizzled by the row so that both the fragment reads (32 rows, same
-// chunk) and the stores of the transposing loader (8 rows apart) hit distinct
-// banks.  MN-contiguous stages are transposed in registers on the way to LDS.
+// Operands may be stored K-contiguous (element (mn, k) at row mn, column k)
+// or MN-contiguous (element (mn, k) at row k, column mn):
+//  - a K-contiguous stage is kept as 256 rows of eight 16-byte chunks, the
+//    chunk index XOR-swizzled by the row, and read with ds_read_b128;
+//  - an MN-contiguous bf16 stage is kept as 64 k-rows of 512 bytes (chunk
+//    index swizzled by the k-row) and read with ds_read_b64_tr_b16, which
+//    hands each lane four K values of one column; two such reads make a
+//    fragment.  f32 stages (32 k-rows of 1 KiB) are read one float at a time.
+// Both swizzles keep every fragment read free of LDS bank conflicts for 32
+// or 64 four-byte banks.
 //
-// Out-of-range rows and K positions are loaded as zeros, so the tile needs
-// no masking in its inner loop; epilogues mask what they write.
+// Loads go through buffer resources whose record count ends at the last
+// valid row, so rows past the operand's extent read as zeros and nothing is
+// read out of bounds; the tile needs no masking in its inner loop.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,149 +35,231 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
-constexpr int kTile = 256;           // block tile along M and along N
-constexpr int kWaveTile = 128;       // wave sub-tile along M and along N
-constexpr int kThreads = 256;        // four waves
-constexpr int kChunks = 8;           // 16-byte K chunks per row per stage
-constexpr int kRowBytes = kChunks * 16;
-constexpr int kOperandBytes = kTile * kRowBytes;    // 32 KiB per operand per stage
-constexpr int kStageBytes = 2 * kOperandBytes;       // A and B
-constexpr int kLdsBytes = 2 * kStageBytes;           // double buffered: 128 KiB
+constexpr int kTile = 256;                 // block tile along M and along N
+constexpr int kWaveTile = 128;             // wave sub-tile along M and along N
+constexpr int kThreads = 256;              // four waves
+constexpr int kStageRowBytes = 128;        // K bytes per row per stage
+constexpr int kSteps = kStageRowBytes / 32;   // k16 (bf16) / k8 (f32) steps per stage
+constexpr int kOperandBytes = kTile * kStageRowBytes;   // 32 KiB per operand per stage
+constexpr int kStageBytes = 2 * kOperandBytes;          // A and B
+constexpr int kStages = 2;                 // stages in LDS (1 in flight while 1 is read)
+constexpr int kLdsBytes = kStages * kStageBytes;        // 128 KiB
+constexpr int kCopiesPerWave = kOperandBytes / 1024 / 4;  // 1 KiB per wave-wide copy
+constexpr uint32_t kOutOfRange = 0x80000000u;           // voffset that reads zeros
+constexpr int kRsrcWord3 = 0x00020000;                  // raw buffer, gfx9 family
 
-template <typename T> struct Elem;
-template <> struct Elem<__bf16> { static constexpr int kPerChunk = 8; };
-template <> struct Elem<float> { static constexpr int kPerChunk = 4; };
-
-// Physical chunk of logical chunk c in LDS row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
-
-__device__ __forceinline__ uint32_t lds_off(int r, int c) {
-  return (uint32_t)(r * kRowBytes + swz(r, c) * 16);
+// Swizzle of a K-contiguous stage: physical chunk = logical chunk ^ swz_k(row).
+__device__ __forceinline__ int swz_k(int r) {
+  return ((r ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1) | (((r >> 1) & 1) << 2);
+}
+// Swizzle of an MN-contiguous bf16 stage: physical chunk = chunk ^ swz_mn(k-row).
+__device__ __forceinline__ int swz_mn(int k) {
+  return ((k & 1) ? 10 : 0) ^ ((k & 2) ? 4 : 0);
 }
 
-// ---------------------------------------------------------------------------
-// Stage loaders: global -> registers (load), registers -> LDS (store).
-// ---------------------------------------------------------------------------
+// Raw buffer descriptor for the byte range [base, base + bytes) (clamped to
+// 4 GiB - 1): 48-bit base, stride 0, record count, gfx9 raw-buffer word 3.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, n, (uint32_t)kRsrcWord3};
+}
 
-// K-contiguous operand.  Thread t copies chunk (t & 7) of rows (t >> 3) + 32 i.
-template <typename T>
-struct LoadK {
-  u32x4_t v[8];
-  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int64_t mn0,
-                                       int64_t mn_ext, int64_t k0, int64_t k_ext, int tid) {
-    const int c = tid & 7;
-    const int64_t k = k0 + (int64_t)c * Elem<T>::kPerChunk;
-    const bool kok = k < k_ext;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t mn = mn0 + (tid >> 3) + 32 * i;
-      if (kok && mn < mn_ext) {
-        v[i] = *reinterpret_cast<const u32x4_t*>(base + mn * ld + k);
-      } else {
-        v[i] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-    const int c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<u32x4_t*>(lds + lds_off(r, c)) = v[i];
-    }
-  }
-};
+// The same range as a compiler-visible buffer resource (for loads and stores
+// whose completion the compiler tracks).  Only the VGPR offset (plus the
+// immediate) is range-checked against the record count, so callers put every
+// row- and column-dependent part of an address there.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer(const void* base, int64_t bytes) {
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
 
-// MN-contiguous operand.
-template <typename T> struct LoadMN;
+// LDS byte address of a pointer into the block's shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
 
-// bf16: thread t loads an 8 (k) x 8 (mn) block: mn chunk (t & 31), k rows
-// 8 (t >> 5) .. +8, and transposes it so that each LDS row (one mn) receives
-// 8 consecutive k values.  mn_ext must be a multiple of 8.
-template <>
-struct LoadMN<__bf16> {
-  u32x4_t v[8];
-  __device__ __forceinline__ void load(const __bf16* __restrict__ base, int64_t ld, int64_t mn0,
-                                       int64_t mn_ext, int64_t k0, int64_t k_ext, int tid) {
-    const int64_t mn = mn0 + (int64_t)(tid & 31) * 8;
-    const bool mok = mn < mn_ext;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t k = k0 + (tid >> 5) * 8 + r;
-      if (mok && k < k_ext) {
-        v[r] = *reinterpret_cast<const u32x4_t*>(base + k * ld + mn);
-      } else {
-        v[r] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-    const int mb = tid & 31;
-    const int kc = tid >> 5;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      // element m of k-row r sits in dword m/2 of v[r], low half if m is even
-      u32x4_t o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t x = v[2 * j][m >> 1];
-        const uint32_t y = v[2 * j + 1][m >> 1];
-        o[j] = (m & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-      }
-      *reinterpret_cast<u32x4_t*>(lds + lds_off(mb * 8 + m, kc)) = o;
-    }
-  }
-};
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (one
+// wave-wide 1 KiB copy).  Issued as inline assembly so that the compiler does
+// not treat later LDS reads as waiting on it: completion is tracked by hand
+// with s_waitcnt vmcnt before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
 
-// f32: thread t loads two 4 (k) x 4 (mn) blocks: mn chunk (t & 63), k chunks
-// (t >> 6) and (t >> 6) + 4.  mn_ext must be a multiple of 4.
-template <>
-struct LoadMN<float> {
-  u32x4_t v[8];
-  __device__ __forceinline__ void load(const float* __restrict__ base, int64_t ld, int64_t mn0,
-                                       int64_t mn_ext, int64_t k0, int64_t k_ext, int tid) {
-    const int64_t mn = mn0 + (int64_t)(tid & 63) * 4;
-    const bool mok = mn < mn_ext;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t k = k0 + ((tid >> 6) + 4 * b) * 4 + r;
-        if (mok && k < k_ext) {
-          v[4 * b + r] = *reinterpret_cast<const u32x4_t*>(base + k * ld + mn);
-        } else {
-          v[4 * b + r] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-    const int mb = tid & 63;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int kc = (tid >> 6) + 4 * b;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        u32x4_t o{v[4 * b + 0][m], v[4 * b + 1][m], v[4 * b + 2][m], v[4 * b + 3][m]};
-        *reinterpret_cast<u32x4_t*>(lds + lds_off(mb * 4 + m, kc)) = o;
-      }
-    }
-  }
-};
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-template <typename T, bool KContig> struct Loader;
-template <typename T> struct Loader<T, true> { typedef LoadK<T> type; };
-template <typename T> struct Loader<T, false> { typedef LoadMN<T> type; };
-
-// Operand in global memory.  For a K-contiguous operand, mn_ext bounds the
-// rows and k_ext the columns; for an MN-contiguous one, the reverse.
+// Operand in global memory.  K-contiguous: mn_ext rows of ld elements, of
+// which the first k_ext are used.  MN-contiguous: k_ext rows of ld elements,
+// of which the first mn_ext are used.
 template <typename T>
 struct Operand {
   const T* base;
   int64_t ld;
   int64_t mn_ext;
   int64_t k_ext;
+};
+
+// ---------------------------------------------------------------------------
+// Stage copies (global -> LDS) and fragment reads (LDS -> registers).
+// ---------------------------------------------------------------------------
+template <typename T, bool KContig> struct Side;
+
+// K-contiguous operand.  Wave w copies rows 8 (8w + i) .. +8 (i < 8): lane l
+// fills physical chunk l % 8 of row 8 (8w + i) + l / 8.
+template <typename T>
+struct Side<T, true> {
+  u32x4_t rsrc;
+  uint32_t voff[kCopiesPerWave];
+  uint32_t kbyte[2];     // byte column of this lane's logical chunk (even / odd copies)
+  int64_t k_ext_bytes;
+  uint32_t frag_off[kSteps];  // per k step: byte offset of this lane's fragment (mi = 0)
+
+  __device__ __forceinline__ void init(const Operand<T>& op, int64_t mn0, int wave, int lane,
+                                       int wsub) {
+    const int64_t row_bytes = op.ld * (int64_t)sizeof(T);
+    rsrc = make_rsrc(op.base + mn0 * op.ld, (op.mn_ext - mn0) * row_bytes);
+    k_ext_bytes = op.k_ext * (int64_t)sizeof(T);
+    const int rsub = lane >> 3;  // 0..7: row within an 8-row copy
+    // swz_k depends on row bits 0..3: bit 3 is the parity of the copy index
+#pragma unroll
+    for (int p = 0; p < 2; ++p) kbyte[p] = (uint32_t)(((lane & 7) ^ swz_k(rsub + 8 * p)) * 16);
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+      const int row = 8 * (kCopiesPerWave * wave + i) + rsub;
+      voff[i] = (uint32_t)(row * row_bytes) + kbyte[i & 1];
+    }
+    const int frow = wsub * kWaveTile + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int ch = 2 * j + (lane >> 5);
+      frag_off[j] = (uint32_t)(frow * kStageRowBytes + ((ch ^ swz_k(frow)) * 16));
+    }
+  }
+  // Copy stage kt (K bytes [kt*128, kt*128 + 128)) to LDS address dst; a dead
+  // copy (live == false) reads zeros.
+  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
+    const uint32_t soff = live ? (uint32_t)(kt * kStageRowBytes) : 0u;
+    const int64_t k0 = kt * kStageRowBytes;
+    const bool ok0 = live && k0 + kbyte[0] < k_ext_bytes;
+    const bool ok1 = live && k0 + kbyte[1] < k_ext_bytes;
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+      const bool ok = (i & 1) ? ok1 : ok0;
+      dma16(rsrc, dst + (kCopiesPerWave * wave + i) * 1024, ok ? voff[i] : kOutOfRange, soff);
+    }
+  }
+  // Fragment of sub-tile mi for k step j of the stage at src.
+  __device__ __forceinline__ u32x4_t frag(const char* src, int mi, int j) const {
+    return *reinterpret_cast<const u32x4_t*>(src + frag_off[j] + mi * 32 * kStageRowBytes);
+  }
+};
+
+// MN-contiguous bf16 operand: a stage is 64 k-rows x 256 mn.  Wave w copies
+// k-rows 2 (8w + i) and +1; lane l fills physical chunk l % 32 of k-row
+// 2 (8w + i) + l / 32.
+template <>
+struct Side<__bf16, false> {
+  const char* base;       // element (mn0, k = 0)
+  int64_t row_bytes;
+  int64_t k_ext;
+  int64_t mn0_bytes;
+  uint32_t voff[kCopiesPerWave];
+  uint32_t frag_off[4];   // per mi: byte offset of this lane's first transposed read
+
+  __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane,
+                                       int wsub) {
+    row_bytes = op.ld * 2;
+    base = reinterpret_cast<const char*>(op.base + mn0);
+    k_ext = op.k_ext;
+    mn0_bytes = mn0 * 2;
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+      const int kr = 2 * (kCopiesPerWave * wave + i) + (lane >> 5);
+      const int c = (lane & 31) ^ swz_mn(kr);
+      voff[i] = (uint32_t)(kr * row_bytes + c * 16);
+    }
+    // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
+    // i % 4 of the 8-byte runs addressed by lanes i / 4 + 4 r (r = 0..3).
+    // Lane jj of group g addresses k-row 8 (g / 2) + jj / 4 (+ 4 for the second
+    // read, + 16 j for k16 step j) and the 4 columns 16 (g % 2) + 4 (jj % 4)
+    // of its 32-column sub-tile, so lane i of the group gets 4 K values of
+    // column 16 (g % 2) + i, as the MFMA operand expects.
+    const int g = lane >> 4, jj = lane & 15;
+    const int kr = 8 * (g >> 1) + (jj >> 2);  // swz_mn depends on kr % 4 only
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int col = wsub * kWaveTile + mi * 32 + 16 * (g & 1) + 4 * (jj & 3);
+      const int c = (col >> 3) ^ swz_mn(kr);
+      frag_off[mi] = (uint32_t)(kr * 512 + c * 16 + (col & 7) * 2);
+    }
+  }
+  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
+    const int64_t k0 = live ? kt * 64 : 0;
+    // base points at column mn0: the record count stops at the operand's last byte
+    const u32x4_t r = make_rsrc(base + k0 * row_bytes, (k_ext - k0) * row_bytes - mn0_bytes);
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+      dma16(r, dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
+    }
+  }
+  __device__ __forceinline__ u32x4_t frag(const char* src, int mi, int j) const {
+    const char* p = src + frag_off[mi] + j * 16 * 512;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p + 4 * 512));
+    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+    const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+    return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+  }
+};
+
+// MN-contiguous f32 operand: a stage is 32 k-rows of 256 floats (1 KiB), one
+// k-row per copy, no swizzle; fragments are read one float at a time.
+template <>
+struct Side<float, false> {
+  const char* base;
+  int64_t row_bytes;
+  int64_t k_ext;
+  int64_t mn0_bytes;
+  uint32_t voff[kCopiesPerWave];
+  uint32_t frag_off;
+
+  __device__ __forceinline__ void init(const Operand<float>& op, int64_t mn0, int wave, int lane,
+                                       int wsub) {
+    row_bytes = op.ld * 4;
+    base = reinterpret_cast<const char*>(op.base + mn0);
+    k_ext = op.k_ext;
+    mn0_bytes = mn0 * 4;
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+      const int kr = kCopiesPerWave * wave + i;
+      voff[i] = (uint32_t)(kr * row_bytes + lane * 16);
+    }
+    frag_off = (uint32_t)((wsub * kWaveTile + (lane & 31)) * 4 + (lane >> 5) * 4 * 1024);
+  }
+  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
+    const int64_t k0 = live ? kt * 32 : 0;
+    const u32x4_t r = make_rsrc(base + k0 * row_bytes, (k_ext - k0) * row_bytes - mn0_bytes);
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+      dma16(r, dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
+    }
+  }
+  // k step j covers k-rows 8 j .. 8 j + 7: lane half h takes rows 8 j + 4 h + q.
+  __device__ __forceinline__ u32x4_t frag(const char* src, int mi, int j) const {
+    const char* p = src + frag_off + mi * 32 * 4 + j * 8 * 1024;
+    u32x4_t v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const uint32_t*>(p + q * 1024);
+    return v;
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -190,10 +279,10 @@ template <>
 struct Mfma<float> {
   // The four floats of a fragment are four successive K steps of 32x32x2; the
   // two lane halves supply the two K values of each step.  A and B use the
-  // same assignment, so every product pairs equal K.
+  // same assignment, so every product pairs equal K.  Each element is copied
+  // to a scalar before the bit cast: a bit cast of a vector-element lvalue
+  // reads element 0 whatever the index.
   __device__ __forceinline__ static f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
-    // Copy each element to a scalar before the bit cast: a bit cast of a
-    // vector-element lvalue reads element 0 whatever the index.
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t ua = a[q];
@@ -216,67 +305,108 @@ __device__ __forceinline__ int acc_row(int mi, int e, int lane) {
   return mi * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
 }
 
+template <typename T, bool AK, bool BK>
+struct Frags {
+  u32x4_t a[4], b[4];
+  __device__ __forceinline__ void read(const Side<T, AK>& sa, const Side<T, BK>& sb,
+                                       const char* stage, int j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = sa.frag(stage, i, j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = sb.frag(stage + kOperandBytes, i, j);
+  }
+  __device__ __forceinline__ void mma(Acc& acc) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn) acc.c[i][jn] = Mfma<T>::run(a[i], b[jn], acc.c[i][jn]);
+  }
+};
+
+// Wait until this wave's copies of all but the newest `Ahead` stages have
+// landed and its own LDS reads are done (vmcnt(n) lgkmcnt(0), gfx9 encoding).
+template <int Ahead>
+__device__ __forceinline__ void wait_stage() {
+  constexpr int n = Ahead * 2 * kCopiesPerWave;  // A and B copies per stage per wave
+  static_assert(n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
 // C[m0:m0+256, n0:n0+256] = sum_k A[m, k] B[n, k] over k in [0, k_len).
+//
+// Every iteration issues exactly one stage of copies, so the number of copies
+// in flight is the same in every iteration and the waits are constants: past
+// the last stage the copies are dead (they read zeros into a buffer that will
+// not be read again).  For stage kt (buffer kt % 2), with fragments of k step
+// j read one step ahead of the MFMAs that use them:
+//   steps 0..2: read step j+1, MFMAs of step j;
+//   wait for stage kt+1 and for the step-3 reads; barrier;
+//   copy stage kt+2 into buffer kt % 2 (every wave is past its last read);
+//   read step 0 of stage kt+1; MFMAs of step 3 of kt.
+// The last stage is peeled off so that the loop body has no branch: a path
+// that skipped the barrier would make the compiler wait for the step-0 reads
+// of the next stage before the step-3 MFMAs.
 template <typename T, bool AK, bool BK>
 __device__ __forceinline__ void tile_mainloop(const Operand<T>& A, const Operand<T>& B,
                                               int64_t m0, int64_t n0, int64_t k_len, char* lds,
                                               Acc& acc) {
-  constexpr int kPer = Elem<T>::kPerChunk;
-  constexpr int64_t kStageK = (int64_t)kChunks * kPer;
+  static_assert(kStages == 2 && kSteps == 4, "pipeline written for two stages of four steps");
+  constexpr int64_t kStageK = kStageRowBytes / sizeof(T);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1;
   const int wn = wave >> 1;
+  const uint32_t lds0 = lds_addr(lds);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc.c[i][j] = f32x16_t{};
 
-  typename Loader<T, AK>::type la;
-  typename Loader<T, BK>::type lb;
+  Side<T, AK> sa;
+  Side<T, BK> sb;
+  sa.init(A, m0, wave, lane, wm);
+  sb.init(B, n0, wave, lane, wn);
   const int64_t nk = (k_len + kStageK - 1) / kStageK;
 
-  la.load(A.base, A.ld, m0, A.mn_ext, 0, A.k_ext, tid);
-  lb.load(B.base, B.ld, n0, B.mn_ext, 0, B.k_ext, tid);
-  la.store(lds, tid);
-  lb.store(lds + kOperandBytes, tid);
-  __syncthreads();
-
-  const int frow_a = wm * kWaveTile + (lane & 31);
-  const int frow_b = wn * kWaveTile + (lane & 31);
-  const int fhalf = lane >> 5;
-
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    char* cur = lds + (kt & 1) * kStageBytes;
-    char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int64_t k0 = (kt + 1) * kStageK;
-      la.load(A.base, A.ld, m0, A.mn_ext, k0, A.k_ext, tid);
-      lb.load(B.base, B.ld, n0, B.mn_ext, k0, B.k_ext, tid);
-    }
 #pragma unroll
-    for (int ks = 0; ks < kChunks / 2; ++ks) {
-      const int ch = 2 * ks + fhalf;
-      u32x4_t fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = *reinterpret_cast<const u32x4_t*>(cur + lds_off(frow_a + 32 * i, ch));
-        fb[i] = *reinterpret_cast<const u32x4_t*>(cur + kOperandBytes + lds_off(frow_b + 32 * i, ch));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc.c[i][j] = Mfma<T>::run(fa[i], fb[j], acc.c[i][j]);
-    }
-    if (more) {
-      la.store(nxt, tid);
-      lb.store(nxt + kOperandBytes, tid);
-    }
-    __syncthreads();
+  for (int s = 0; s < kStages; ++s) {
+    const uint32_t dst = lds0 + s * kStageBytes;
+    sa.copy(dst, s, wave, s < nk);
+    sb.copy(dst + kOperandBytes, s, wave, s < nk);
   }
+  wait_stage<kStages - 1>();
+  block_barrier();
+
+  Frags<T, AK, BK> f0, f1;
+  f0.read(sa, sb, lds, 0);
+  for (int64_t kt = 0; kt + 1 < nk; ++kt) {
+    const int64_t buf = kt & 1;
+    const char* cur = lds + buf * kStageBytes;
+    f1.read(sa, sb, cur, 1);
+    f0.mma(acc);
+    f0.read(sa, sb, cur, 2);
+    f1.mma(acc);
+    f1.read(sa, sb, cur, 3);
+    f0.mma(acc);
+    wait_stage<0>();
+    block_barrier();
+    const uint32_t dst = lds0 + (uint32_t)(buf * kStageBytes);
+    sa.copy(dst, kt + 2, wave, kt + 2 < nk);
+    sb.copy(dst + kOperandBytes, kt + 2, wave, kt + 2 < nk);
+    f0.read(sa, sb, lds + (buf ^ 1) * kStageBytes, 0);
+    f1.mma(acc);
+  }
+  const char* last = lds + ((nk - 1) & 1) * kStageBytes;
+  f1.read(sa, sb, last, 1);
+  f0.mma(acc);
+  f0.read(sa, sb, last, 2);
+  f1.mma(acc);
+  f1.read(sa, sb, last, 3);
+  f0.mma(acc);
+  f1.mma(acc);
+  wait_stage<0>();  // no copy may still be writing LDS when the block exits
 }
 
 }  // namespace lce
