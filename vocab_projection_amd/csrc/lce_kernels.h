@@ -39,7 +39,6 @@ struct GemmArgs {
   const T* b; int64_t ldb, b_mn_ext, b_k_ext;
   int64_t k_len;
   float* c; int64_t ldc, m, n;
-  int accumulate;
   int64_t m_tiles, n_tiles, group_m;  // tile order, set by the launcher
 };
 

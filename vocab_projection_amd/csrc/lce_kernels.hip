@@ -130,26 +130,38 @@ __global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) 
 // ---------------------------------------------------------------------------
 // Backward strip: same tile, epilogue writes G[tok, v] = scale*(p - onehot).
 // ---------------------------------------------------------------------------
-// Four consecutive gradient values of one token row, stored with one buffer
-// store (8 bytes of bf16 or 16 bytes of f32) at byte offset voff of the row.
+// Four consecutive gradient values of one token row, packed in the strip's
+// element type (8 bytes of bf16, rounded to nearest even, or 16 bytes of f32).
 template <typename T> struct GPack;
 template <> struct GPack<__bf16> {
-  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, float a,
-                                               float b, float c, float d) {
+  typedef u32x2_t type;
+  __device__ __forceinline__ static type pack(float a, float b, float c, float d) {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
     const bf16x2_t lo{(__bf16)a, (__bf16)b};
     const bf16x2_t hi{(__bf16)c, (__bf16)d};
-    const u32x2_t v{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
+    return type{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
   }
 };
 template <> struct GPack<float> {
-  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t r, uint32_t voff, float a,
-                                               float b, float c, float d) {
-    const u32x4_t v{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
-                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+  typedef u32x4_t type;
+  __device__ __forceinline__ static type pack(float a, float b, float c, float d) {
+    return type{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
   }
+};
+
+// The gradient strip leaves through LDS in passes of kGradTok tokens: the
+// waves holding those tokens write their G values as token rows, then every
+// thread stores whole 16-byte runs of a row, so a wave writes 512 (bf16) or
+// 1024 (f32) contiguous bytes of G per instruction.
+template <typename T> struct GradStage {
+  static constexpr int kTok = sizeof(T) == 2 ? 128 : 64;      // tokens per pass
+  static constexpr int kRowBytes = kTile * (int)sizeof(T);      // 256 vocabulary columns
+  static constexpr int kStride = kRowBytes + 16;                // padded LDS row
+  static constexpr int kRunsPerRow = kRowBytes / 16;
+  static constexpr int kRowsPerSweep = kThreads / kRunsPerRow;
+  static constexpr int kSweeps = kTok / kRowsPerSweep;
+  static_assert(kTok * kStride <= kLdsBytes, "staging fits in LDS");
 };
 
 template <typename T>
@@ -162,50 +174,92 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
   Acc acc;
   tile_mainloop<T, true, true>(A, B, m0, n0, a.H, lds, acc);
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  typedef GradStage<T> S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t vrow0 = m0 + wm * kWaveTile;
+  const bool full = vrow0 + kWaveTile <= a.v_len;  // no strip rows past v_len in this wave
   const float scale_all = a.ctrl->grad_scale;
-  // G rows n0.. of the strip buffer, from column m0: byte offset
+  // G rows n0.. of the strip buffer from column m0: byte offset
   // (tok - n0) * ldg * elt + (col - m0) * elt; rows past N are out of range.
   const int64_t row_bytes = a.ldg * (int64_t)sizeof(T);
   const __amdgpu_buffer_rsrc_t gbuf = make_buffer(
       a.g_strip + n0 * a.ldg + m0, (a.N - n0) * row_bytes - m0 * (int64_t)sizeof(T));
+  constexpr int kNiPerPass = S::kTok / 32 > 4 ? 4 : S::kTok / 32;
 
+  // G for every element, in place (all waves at once).
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
-    const int tok_local = wn * kWaveTile + ni * 32 + (lane & 31);
-    const int64_t tok = n0 + tok_local;
+    const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
     const bool tok_ok = tok < a.N;
     const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
     const float sc = t != a.ignore_index ? scale_all : 0.f;
     const float lse2 = (tok_ok ? a.lse[tok] : 0.f) * kLog2e;
-    const int64_t tl = (int64_t)t - (a.v_begin + vrow0);  // target row within this wave
-    const uint32_t vbase = (uint32_t)(tok_local * row_bytes) +
-                           (uint32_t)((wm * kWaveTile + (lane >> 5) * 4) * sizeof(T));
+    const int64_t tl64 = (int64_t)t - (a.v_begin + vrow0);  // target row in this wave
+    const bool hit = t != a.ignore_index && tl64 >= 0 && tl64 < kWaveTile;
+    const int tl = hit ? (int)tl64 : -1;
+    const bool any_hit = __any(hit);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float g[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = acc_row(mi, 4 * q + i, lane);
-          float p = sc * fast_exp2(__builtin_fmaf(acc.c[mi][ni][4 * q + i], kLog2e, -lse2));
-          p = (vrow0 + r < a.v_len) ? p : 0.f;
-          g[i] = (r == tl) ? p - sc : p;
-        }
-        GPack<T>::store(gbuf, vbase + (uint32_t)((mi * 32 + q * 8) * sizeof(T)), g[0], g[1], g[2],
-                        g[3]);
+      for (int e = 0; e < 16; ++e) {
+        const int r = acc_row(mi, e, lane);
+        float g = sc * fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, -lse2));
+        if (!full) g = (vrow0 + r < a.v_len) ? g : 0.f;
+        if (any_hit) g = (r == tl) ? g - sc : g;
+        acc.c[mi][ni][e] = g;
       }
+  }
+
+#pragma unroll
+  for (int pass = 0; pass < kTile / S::kTok; ++pass) {
+    block_barrier();  // LDS free: main loop reads (pass 0) or previous pass done
+    const int tok_base = pass * S::kTok;  // first token of the pass within the tile
+    if (wn == tok_base / kWaveTile) {
+#pragma unroll
+      for (int nj = 0; nj < kNiPerPass; ++nj) {
+        const int ni = (tok_base % kWaveTile) / 32 + nj;
+        const int tok_local = wn * kWaveTile + ni * 32 + (lane & 31);
+        char* lrow = lds + (tok_local - tok_base) * S::kStride +
+                     (wm * kWaveTile + (lane >> 5) * 4) * (int)sizeof(T);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16_t& c = acc.c[mi][ni];
+            *reinterpret_cast<typename GPack<T>::type*>(lrow + (mi * 32 + q * 8) * (int)sizeof(T)) =
+                GPack<T>::pack(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+          }
+      }
+    }
+    block_barrier();
+    const int run = tid % S::kRunsPerRow;
+#pragma unroll
+    for (int i = 0; i < S::kSweeps; ++i) {
+      const int row = tid / S::kRunsPerRow + S::kRowsPerSweep * i;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + row * S::kStride + run * 16);
+      const uint32_t off = (uint32_t)((tok_base + row) * row_bytes) + run * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(v, gbuf, off, 0, 0);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Plain fp32-output GEMM tile: C[m, n] (+)= sum_k A[m, k] B[n, k].
+//
+// The epilogue goes through LDS (free once the main loop is done) in four
+// passes of 64 rows: the two waves that hold those rows write them, then all
+// 256 threads move whole 16-byte runs of each row, so that every wave reads
+// and writes 1 KiB of one row of C per instruction, and a pass issues all its
+// loads (read-modify-write for Accum) before any add.
 // ---------------------------------------------------------------------------
-template <typename T, bool AK, bool BK>
+constexpr int kEpiRows = 64;                       // rows of C per pass
+constexpr int kEpiStride = kTile * 4 + 16;          // padded LDS row (bytes)
+static_assert(kEpiRows * kEpiStride <= kLdsBytes, "epilogue staging fits in LDS");
+
+template <typename T, bool AK, bool BK, bool Accum>
 __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   int64_t m0, n0;
@@ -215,37 +269,63 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g)
   Acc acc;
   tile_mainloop<T, AK, BK>(A, B, m0, n0, g.k_len, lds, acc);
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   // C from (m0, n0): byte offset (row - m0) * ldc * 4 + (col - n0) * 4.  Rows
-  // past m fall past the record count; columns past n get an out-of-range
-  // offset, since they would otherwise land in the next row.
+  // past m fall past the record count; 16-byte runs past n get an
+  // out-of-range offset (n is a multiple of 4, so runs are never split).
   const uint32_t ldc4 = (uint32_t)(g.ldc * 4);
   const __amdgpu_buffer_rsrc_t cbuf =
       make_buffer(g.c + m0 * g.ldc + n0, (g.m - m0) * g.ldc * 4 - n0 * 4);
-  uint32_t vcol[4];
+  const int run = tid & 63;                         // 16-byte run of a row (4 columns)
+  const bool run_ok = n0 + 4 * run < g.n;
+  constexpr int kRowsPerThread = kEpiRows / 4;      // 4 waves, one row each at a time
+
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int col = wn * kWaveTile + ni * 32 + (lane & 31);
-    vcol[ni] = n0 + col < g.n ? (uint32_t)((wm * kWaveTile + (lane >> 5) * 4) * ldc4 + col * 4)
-                              : kOutOfRange;
-  }
+  for (int pass = 0; pass < kTile / kEpiRows; ++pass) {
+    block_barrier();  // LDS free: main loop reads (pass 0) or previous pass done
+    if (wm == pass / 2) {
+      // rows (pass % 2) * 64 .. +64 of this wave's 128 = sub-tiles mi = 2 (pass % 2) + {0, 1}
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+      for (int h = 0; h < 2; ++h) {
+        const int mi = 2 * (pass % 2) + h;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t roff = (uint32_t)(mi * 32 + (e >> 2) * 8 + (e & 3)) * ldc4;
+        for (int ni = 0; ni < 4; ++ni) {
+          const int col = wn * kWaveTile + ni * 32 + (lane & 31);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const uint32_t off = vcol[ni] + roff;
-        float v = acc.c[mi][ni][e];
-        if (g.accumulate) {
-          v += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cbuf, off, 0, 0));
+          for (int e = 0; e < 16; ++e) {
+            const int row = h * 32 + acc_row(0, e, lane);
+            *reinterpret_cast<float*>(lds + row * kEpiStride + col * 4) = acc.c[mi][ni][e];
+          }
         }
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), cbuf, off, 0, 0);
       }
     }
+    block_barrier();
+    f32x4_t v[kRowsPerThread];
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int row = wave + 4 * i;
+      v[i] = *reinterpret_cast<const f32x4_t*>(lds + row * kEpiStride + run * 16);
+    }
+    const int row0 = pass * kEpiRows;
+    if (Accum) {
+      u32x4_t old[kRowsPerThread];
+#pragma unroll
+      for (int i = 0; i < kRowsPerThread; ++i) {
+        const uint32_t off = run_ok ? (uint32_t)(row0 + wave + 4 * i) * ldc4 + run * 16 : kOutOfRange;
+        old[i] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, off, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kRowsPerThread; ++i) v[i] += __builtin_bit_cast(f32x4_t, old[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const uint32_t off = run_ok ? (uint32_t)(row0 + wave + 4 * i) * ldc4 + run * 16 : kOutOfRange;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v[i]), cbuf, off, 0, 0);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -379,16 +459,17 @@ hipError_t launch_strip_grad(StripArgs<T> a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, bool AK, bool BK>
+template <typename T, bool AK, bool BK, bool Accum>
 static hipError_t launch_gemm(GemmArgs<T> g, hipStream_t st) {
   g.m_tiles = cdiv(g.m, kTile);
   g.n_tiles = cdiv(g.n, kTile);
   g.group_m = kGemmGroupM;
   const int64_t blocks = g.m_tiles * g.n_tiles;
-  hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&gemm_f32out_kernel<T, AK, BK>));
+  hipError_t e =
+      set_lds<T>(reinterpret_cast<const void*>(&gemm_f32out_kernel<T, AK, BK, Accum>));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_f32out_kernel<T, AK, BK>), dim3((unsigned)blocks), dim3(kThreads),
-                     kLdsBytes, st, g);
+  hipLaunchKernelGGL((gemm_f32out_kernel<T, AK, BK, Accum>), dim3((unsigned)blocks),
+                     dim3(kThreads), kLdsBytes, st, g);
   return hipGetLastError();
 }
 
@@ -400,8 +481,9 @@ hipError_t launch_dh(const T* g_strip, int64_t ldg, const T* w_strip, int64_t v_
   g.a = g_strip; g.lda = ldg; g.a_mn_ext = n_tok; g.a_k_ext = v_len;   // K-contiguous
   g.b = w_strip; g.ldb = h;   g.b_mn_ext = h;     g.b_k_ext = v_len;   // MN-contiguous
   g.k_len = v_len;
-  g.c = d_hidden; g.ldc = h; g.m = n_tok; g.n = h; g.accumulate = accumulate;
-  return launch_gemm<T, true, false>(g, st);
+  g.c = d_hidden; g.ldc = h; g.m = n_tok; g.n = h;
+  return accumulate ? launch_gemm<T, true, false, true>(g, st)
+                    : launch_gemm<T, true, false, false>(g, st);
 }
 
 // dW_s[v_len, H] = G[:, :v_len]^T . h: M = strip rows, N = H, K = tokens.
@@ -413,8 +495,8 @@ hipError_t launch_dw(const T* g_strip, int64_t ldg, const T* hidden, int64_t v_l
   g.a = g_strip; g.lda = ldg; g.a_mn_ext = cols; g.a_k_ext = n_tok;    // MN-contiguous
   g.b = hidden;  g.ldb = h;   g.b_mn_ext = h;    g.b_k_ext = n_tok;    // MN-contiguous
   g.k_len = n_tok;
-  g.c = d_weight_strip; g.ldc = h; g.m = v_len; g.n = h; g.accumulate = 0;
-  return launch_gemm<T, false, false>(g, st);
+  g.c = d_weight_strip; g.ldc = h; g.m = v_len; g.n = h;
+  return launch_gemm<T, false, false, false>(g, st);
 }
 
 hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st) {
