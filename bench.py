@@ -183,6 +183,33 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+KERNEL_SOURCES = ("tile_engine.h", "lce_kernels.hip", "lce_kernels.h")
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "vocab_projection_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, step: str):
+    """HBM bytes per launch of `step` from the committed FETCH_SIZE / WRITE_SIZE
+    summary (already scaled by the copy-kernel calibration), or None when there
+    is none for this workload or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    if prof.get("source_sha256") != kernel_source_sha256():
+        return None
+    k = prof.get("kernels", {}).get(step)
+    return None if k is None else k["hbm_bytes_per_dispatch"]
+
+
 def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, loss, peak):
     """Run the same steps through the step-level calls with an event pair around
     every kernel launch of the fold loops; return per-kernel times and the
@@ -231,7 +258,8 @@ def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, 
     dom = max(flops_per_row, key=lambda k: out[k]["total_ms_per_step"])
     achieved = out[dom]["tflops"]
     roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None, "kernel": out[dom]["kernel"],
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, dom),
+            "kernel": out[dom]["kernel"],
             "step": dom, "avg_launch_ms": out[dom]["avg_ms"],
             "algorithmic_flop_per_launch": out[dom]["algorithmic_flop_per_launch"]}
     log("per-kernel:", json.dumps(out))
