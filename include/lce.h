@@ -63,10 +63,10 @@ typedef enum lce_reduction {
  * strip (Vs) is the widest vocabulary slice folded per step; it fixes the
  * workspace size.  0 selects lce_pick_strip(p, LCE_DEFAULT_BUDGET). */
 typedef struct lce_problem {
-  int64_t n_tokens;     /* N >= 1 */
-  int64_t hidden;       /* H >= 1 */
-  int64_t vocab;        /* V >= 1 */
-  int64_t strip;        /* Vs in [1, V], or 0 */
+  int64_t n_tokens;     /* N in [1, 2^31] */
+  int64_t hidden;       /* H in [1, 2^20] */
+  int64_t vocab;        /* V in [1, 2^31] */
+  int64_t strip;        /* Vs in [1, min(V, 2^21)], or 0 */
   int32_t dtype;        /* lce_dtype_t of hidden and weight */
   int32_t reduction;    /* lce_reduction_t */
   int32_t ignore_index; /* rows with this target are left out */
@@ -80,7 +80,7 @@ const char* lce_status_string(lce_status_t s);
 
 /* Widest strip width Vs whose workspace fits in budget_bytes: a multiple of
  * 256 (the kernels' vocabulary tile), at least 256, at most V rounded up to
- * 256, then clamped to V.  Follows from the second page's section 3.5 (device
+ * 256 and at most 2^21, then clamped to V.  Follows from the second page's section 3.5 (device
  * working sets fixed by the launch configuration, checkable before launch).
  * Returns -1 for an invalid problem. p->strip is ignored. */
 int64_t lce_pick_strip(const lce_problem_t* p, size_t budget_bytes);

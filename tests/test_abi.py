@@ -88,6 +88,12 @@ def test_problem_validation(lib):
     assert lib.lce_workspace_bytes(ctypes.byref(p)) == 0
     assert lib.lce_workspace_bytes(ctypes.byref(P(h=12))) == 0          # bf16 needs H % 8 == 0
     assert lib.lce_workspace_bytes(ctypes.byref(P(h=12, dtype=torch.float32))) > 0
+    # tile offsets stay below 2^31: H <= 2^20, strip <= 2^21
+    assert lib.lce_workspace_bytes(ctypes.byref(P(n=4, h=1 << 20, v=300))) > 0
+    assert lib.lce_workspace_bytes(ctypes.byref(P(n=4, h=(1 << 20) + 8, v=300))) == 0
+    assert lib.lce_workspace_bytes(ctypes.byref(P(n=4, h=8, v=1 << 23, strip=1 << 21))) > 0
+    assert lib.lce_workspace_bytes(ctypes.byref(P(n=4, h=8, v=1 << 23, strip=(1 << 21) + 1))) == 0
+    assert B.lce_pick_strip(P(n=1, h=8, v=1 << 24), 1 << 50) == 1 << 21
 
 
 def _call_fwd(lib, p, ws_bytes, ptrs):

@@ -46,12 +46,15 @@ def to_gpu(w, hid, wt, t):
             torch.from_numpy(t).to(DEV))
 
 
-def run_hip(w, h, W, t, *, strip=None, order=None, grad_out=None):
+def run_hip(w, h, W, t, *, strip=None, order=None, grad_out=None, poison=False):
     """Forward + backward through the C ABI; order=None uses lce_forward/lce_backward,
-    otherwise the strip-level calls in the given (v_begin, v_len) order."""
+    otherwise the strip-level calls in the given (v_begin, v_len) order.  With
+    poison=True the workspace starts as all-ones bytes (NaN in bf16 and f32)."""
     vs = strip or w.strip
     p = B.make_problem(h, W, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, strip=vs)
     ws = B.workspace(p, DEV)
+    if poison:
+        ws.fill_(255)
     go = torch.tensor([w.grad_out if grad_out is None else grad_out], dtype=torch.float32,
                       device=DEV)
     loss = torch.empty(1, dtype=torch.float32, device=DEV)
@@ -197,6 +200,30 @@ def test_out_of_range_target_gives_nan_loss():
     h, W, tt = to_gpu(w, S.hidden(w), S.weight(w), t)
     o = run_hip(w, h, W, tt)
     assert math.isnan(o["loss"]) and math.isnan(o["row_loss"][3])
+
+
+def test_strip_buffer_over_2gib_with_ragged_tail():
+    """A gradient strip of 131072 x 8448 bf16 (2.2 GB, past 2^31 bytes) and a last
+    strip of 100 rows (not a multiple of the 64-element K stage), on a workspace
+    that starts as NaN bytes: lanes masked past the strip must read zeros."""
+    w = S.small("bf16_big_strip_tail", 131072, 64, 8548, 8448, ignore_frac=0.05)
+    hid, wt, t = S.hidden(w), S.weight(w), S.targets(w)
+    h, W, tt = to_gpu(w, hid, wt, t)
+    out = run_hip(w, h, W, tt, poison=True)
+    for k in ("dh", "dw"):
+        assert torch.isfinite(out[k]).all().item(), k
+    loss, lse, _ = O.forward(hid, wt, t, ignore_index=S.IGNORE_INDEX, reduction=w.reduction,
+                             row_chunk=8192)
+    assert_loss(w, out["loss"], loss)
+    assert_lse(out["lse"], lse)
+    rng = np.random.default_rng(5)
+    rows = sample_rows(w, t, rng, 128)
+    sc = O.grad_scale(t, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, grad_out=w.grad_out)
+    assert_grad(w, out["dh"][torch.from_numpy(rows).to(DEV)].cpu().numpy(),
+                O.hidden_grad_rows(hid[rows], wt, t[rows], sc[rows]), "dH rows")
+    vids = np.unique(np.concatenate([np.arange(8448 - 4, 8548), rng.choice(8448, 64, replace=False)]))
+    assert_grad(w, out["dw"][torch.from_numpy(vids).to(DEV)].cpu().numpy(),
+                O.weight_grad_rows(hid, wt[vids], vids, t, lse, sc), "dW rows")
 
 
 def test_autograd_function():

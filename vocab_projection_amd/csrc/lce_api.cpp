@@ -15,6 +15,8 @@ namespace {
 constexpr int64_t kStripTile = 256;  // vocabulary tile of the strip kernels
 constexpr int64_t kPartRows = 128;   // vocabulary rows per forward partial
 constexpr size_t kHeader = 256;
+constexpr int64_t kMaxHidden = 1LL << 20;
+constexpr int64_t kMaxStrip = 1LL << 21;
 
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
@@ -33,8 +35,12 @@ bool problem_ok(const lce_problem_t* p) {
   if (p->dtype != LCE_F32 && p->dtype != LCE_BF16) return false;
   if (p->reduction != LCE_MEAN && p->reduction != LCE_SUM) return false;
   if (p->reserved != 0) return false;
-  // keep every index and byte offset far inside int64
-  if (p->n_tokens > (1LL << 31) || p->hidden > (1LL << 24) || p->vocab > (1LL << 31)) return false;
+  // The kernels address one tile with byte offsets below 2^31: at most 256
+  // rows of H elements or of a strip row of round_up(Vs, 256) elements, at
+  // most 4 bytes each.  H <= 2^20 and Vs <= 2^21 keep 256 * 4 * max(H, Vs)
+  // within 2^31.
+  if (p->n_tokens > (1LL << 31) || p->hidden > kMaxHidden || p->vocab > (1LL << 31)) return false;
+  if (p->strip > kMaxStrip) return false;
   return true;
 }
 
@@ -63,6 +69,7 @@ int64_t pick_strip(const lce_problem_t* p, size_t budget) {
     if (tiles * kStripTile > vs) vs = tiles * kStripTile;
   }
   if (vs > vmax) vs = vmax;
+  if (vs > kMaxStrip) vs = kMaxStrip;
   if (vs > p->vocab) vs = p->vocab;
   return vs;
 }

@@ -59,12 +59,20 @@ __device__ __forceinline__ int swz_mn(int k) {
   return ((k & 1) ? 10 : 0) ^ ((k & 2) ? 4 : 0);
 }
 
-// Raw buffer descriptor for the byte range [base, base + bytes) (clamped to
-// 4 GiB - 1): 48-bit base, stride 0, record count, gfx9 raw-buffer word 3.
+// Record count of a descriptor for `bytes` bytes, capped at 2^31 so that the
+// out-of-range offset kOutOfRange (2^31) is always past the end.  Every tile
+// addresses at most 256 rows of at most 8 MiB (the host limits H <= 2^20 and
+// strip <= 2^21), i.e. offsets below 2^31, so the cap never hides valid data.
+__device__ __forceinline__ uint32_t record_count(int64_t bytes) {
+  return bytes <= 0 ? 0u : (bytes >= (int64_t)kOutOfRange ? kOutOfRange : (uint32_t)bytes);
+}
+
+// Raw buffer descriptor for the byte range [base, base + bytes): 48-bit base,
+// stride 0, record count, gfx9 raw-buffer word 3.
 __device__ __forceinline__ u32x4_t make_rsrc(const void* base, int64_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
-  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, n, (uint32_t)kRsrcWord3};
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, record_count(bytes),
+                 (uint32_t)kRsrcWord3};
 }
 
 // The same range as a compiler-visible buffer resource (for loads and stores
@@ -72,8 +80,8 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, int64_t bytes) {
 // immediate) is range-checked against the record count, so callers put every
 // row- and column-dependent part of an address there.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer(const void* base, int64_t bytes) {
-  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)record_count(bytes), kRsrcWord3);
 }
 
 // LDS byte address of a pointer into the block's shared memory.
