@@ -86,8 +86,9 @@ const char* lce_status_string(lce_status_t s);
 int64_t lce_pick_strip(const lce_problem_t* p, size_t budget_bytes);
 
 /* Workspace bytes needed by every call below for problem p (with its strip,
- * or the default policy when p->strip == 0): one gradient strip
- * N x round_up(Vs, 256) elements plus 12 bytes per token and a small header.
+ * or the default policy when p->strip == 0): one gradient strip of
+ * N x round_up(Vs, 256) elements plus a 256-byte header (the forward keeps its
+ * partials and running state inside the strip region).
  * Returns 0 for an invalid problem. */
 size_t lce_workspace_bytes(const lce_problem_t* p);
 

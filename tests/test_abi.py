@@ -49,19 +49,21 @@ def P(n=64, h=64, v=1000, dtype=torch.bfloat16, **kw):
 
 
 def test_workspace_formula(lib):
+    """One strip of N x round_up(Vs, 256) elements plus a 256-byte header."""
     p = P(131072, 2048, 151936, strip=8192)
-    col = (4 * 131072 + 255) // 256 * 256
-    assert B.lce_workspace_bytes(p) == 256 + 3 * col + 131072 * 8192 * 2
+    assert B.lce_workspace_bytes(p) == 256 + 131072 * 8192 * 2
     p = P(256, 128, 1024, torch.float32, strip=256)
-    assert B.lce_workspace_bytes(p) == 256 + 3 * 1024 + 256 * 256 * 4
+    assert B.lce_workspace_bytes(p) == 256 + 256 * 256 * 4
     p = P(100, 64, 1000, strip=300)  # strip buffer rounds the strip up to 256 columns
-    assert B.lce_workspace_bytes(p) == 256 + 3 * 512 + 100 * 512 * 2
+    assert B.lce_workspace_bytes(p) == 256 + 100 * 512 * 2
+    p = P(1, 8, 1, strip=1)  # one token: the forward's partials + state (16 + 3*256) win
+    assert B.lce_workspace_bytes(p) == 256 + 16 + 3 * 256
 
 
 def test_pick_strip_policy(lib):
     n = 131072
     p = P(n, 2048, 151936)
-    fixed = 256 + 3 * ((4 * n + 255) // 256 * 256)
+    fixed = 256
     vs = B.lce_pick_strip(p, fixed + n * 2 * 8192)
     assert vs == 8192
     assert B.lce_pick_strip(p, fixed + n * 2 * 8192 - 1) == 8192 - 256

@@ -46,15 +46,23 @@ bool problem_ok(const lce_problem_t* p) {
 
 size_t elt_of(int dtype) { return dtype == LCE_BF16 ? 2 : 4; }
 
-size_t fixed_bytes(int64_t n) {
-  return kHeader + 3 * (size_t)round_up(4 * n, 256);
-}
+// Workspace: a 256-byte control block, then one strip region of N x ldg
+// elements.  The backward keeps its gradient strip G there; the forward keeps
+// its per-block partials [ldg / 128, N] of (max, sum) there, followed by the
+// running per-token state (max, sum, target logit), each column padded to 256
+// bytes.  The region is the larger of the two needs; the forward's is smaller
+// except for a handful of tokens.
+size_t state_col_bytes(int64_t n) { return (size_t)round_up(4 * n, 256); }
+
+size_t partial_bytes(int64_t n, int64_t ldg) { return (size_t)n * (size_t)(ldg / kPartRows) * 8; }
+
+size_t fixed_bytes(int64_t) { return kHeader; }
 
 size_t bytes_for_strip(int64_t n, int64_t vs, size_t elt) {
   const int64_t ldg = round_up(vs, kStripTile);
-  const size_t g = (size_t)n * (size_t)ldg * elt;                   // backward G strip
-  const size_t part = (size_t)n * (size_t)(ldg / kPartRows) * 8;    // forward partials
-  return fixed_bytes(n) + (g > part ? g : part);
+  const size_t g = (size_t)n * (size_t)ldg * elt;                            // backward G strip
+  const size_t fwd = partial_bytes(n, ldg) + 3 * state_col_bytes(n);      // forward use
+  return kHeader + (g > fwd ? g : fwd);
 }
 
 int64_t pick_strip(const lce_problem_t* p, size_t budget) {
@@ -62,7 +70,7 @@ int64_t pick_strip(const lce_problem_t* p, size_t budget) {
   const int64_t n = p->n_tokens;
   const int64_t vmax = round_up(p->vocab, kStripTile);
   int64_t vs = kStripTile;
-  const size_t fixed = fixed_bytes(n);
+  const size_t fixed = fixed_bytes(n);  // the strip region holds everything else
   if (budget > fixed) {
     const size_t per_tile = (size_t)n * (size_t)kStripTile * elt;
     const int64_t tiles = (int64_t)((budget - fixed) / per_tile);
@@ -87,11 +95,11 @@ lce_status_t make_plan(const lce_problem_t* p, Plan* pl) {
   pl->reduction = p->reduction;
   pl->ignore_index = p->ignore_index;
   pl->elt = elt;
-  const size_t col = (size_t)round_up(4 * pl->N, 256);
-  pl->off_m = kHeader;
+  const size_t col = state_col_bytes(pl->N);
+  pl->off_strip = kHeader;
+  pl->off_m = pl->off_strip + partial_bytes(pl->N, pl->ldg);
   pl->off_s = pl->off_m + col;
   pl->off_zt = pl->off_s + col;
-  pl->off_strip = pl->off_zt + col;
   pl->total = bytes_for_strip(pl->N, pl->Vs, elt);
   return LCE_OK;
 }
