@@ -1,22 +1,27 @@
 // tile_engine.h - one 256x256 MFMA tile of C = A . B^T on gfx950 (CDNA4).
 //
 // A block of 256 threads (four wave64s in a 2x2 grid, each owning a 128x128
-// sub-tile of fp32 accumulators) walks K in stages of 128 bytes per row:
-// 64 bf16 or 32 f32 elements, so that every global request is a whole
-// 128-byte line.  Stages are copied from global memory straight into LDS with
-// buffer_load ... lds (no register staging), two stages deep (2 x 64 KiB):
-// the next stage is in flight while one is read.
+// sub-tile of fp32 accumulators) walks K in stages of 64 bytes per row (32
+// bf16 or 16 f32 elements).  Stages are copied from global memory straight
+// into LDS with buffer_load ... lds (no register staging) into a ring of
+// kStages buffers, so a stage is copied kStages - 1 stages before it is read.
+// The copies of a stage are spread over the MFMAs of the stage before: one
+// wave-wide copy after every fourth MFMA.  The texture unit takes many cycles
+// per 1 KiB copy and is shared by the CU's four waves, so copies issued in a
+// burst stall every wave's MFMA issue at once; spread out, they hide behind
+// the MFMAs.  The lead given by the ring is what lets them be spread.
 // Fragments are read back from LDS as 16-byte K-runs that feed
-// v_mfma_f32_32x32x16_bf16 (bf16) or four v_mfma_f32_32x32x2_f32 (f32).
+// v_mfma_f32_32x32x16_bf16 (bf16) or four v_mfma_f32_32x32x2_f32 (f32), one
+// k step ahead of their MFMAs.
 //
 // Operands may be stored K-contiguous (element (mn, k) at row mn, column k)
 // or MN-contiguous (element (mn, k) at row k, column mn):
-//  - a K-contiguous stage is kept as 256 rows of eight 16-byte chunks, the
+//  - a K-contiguous stage is kept as 256 rows of four 16-byte chunks, the
 //    chunk index XOR-swizzled by the row, and read with ds_read_b128;
-//  - an MN-contiguous bf16 stage is kept as 64 k-rows of 512 bytes (chunk
+//  - an MN-contiguous bf16 stage is kept as 32 k-rows of 512 bytes (chunk
 //    index swizzled by the k-row) and read with ds_read_b64_tr_b16, which
 //    hands each lane four K values of one column; two such reads make a
-//    fragment.  f32 stages (32 k-rows of 1 KiB) are read one float at a time.
+//    fragment.  f32 stages (16 k-rows of 1 KiB) are read one float at a time.
 // Both swizzles keep every fragment read free of LDS bank conflicts for 32
 // or 64 four-byte banks.
 //
@@ -40,19 +45,29 @@ typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 constexpr int kTile = 256;                 // block tile along M and along N
 constexpr int kWaveTile = 128;             // wave sub-tile along M and along N
 constexpr int kThreads = 256;              // four waves
-constexpr int kStageRowBytes = 128;        // K bytes per row per stage
+constexpr int kStageRowBytes = 64;         // K bytes per row per stage
 constexpr int kSteps = kStageRowBytes / 32;   // k16 (bf16) / k8 (f32) steps per stage
-constexpr int kOperandBytes = kTile * kStageRowBytes;   // 32 KiB per operand per stage
+constexpr int kChunks = kStageRowBytes / 16;  // 16-byte chunks per row per stage
+constexpr int kOperandBytes = kTile * kStageRowBytes;   // per operand per stage
 constexpr int kStageBytes = 2 * kOperandBytes;          // A and B
-constexpr int kStages = 2;                 // stages in LDS (1 in flight while 1 is read)
-constexpr int kLdsBytes = kStages * kStageBytes;        // 128 KiB
+constexpr int kStages = 4;                 // ring of stages in LDS
+constexpr int kLdsBytes = kStages * kStageBytes;
 constexpr int kCopiesPerWave = kOperandBytes / 1024 / 4;  // 1 KiB per wave-wide copy
+constexpr int kRowsPerCopy = 1024 / kStageRowBytes;       // K-contiguous rows per copy
+static_assert(kStageRowBytes == 64 || kStageRowBytes == 128, "stage of 64 or 128 bytes per row");
+static_assert(kSteps % 2 == 0, "fragments alternate between two register sets");
+static_assert(kStages >= 2 && kLdsBytes <= 160 * 1024, "ring fits in LDS");
 constexpr uint32_t kOutOfRange = 0x80000000u;           // voffset that reads zeros
 constexpr int kRsrcWord3 = 0x00020000;                  // raw buffer, gfx9 family
 
-// Swizzle of a K-contiguous stage: physical chunk = logical chunk ^ swz_k(row).
+// Swizzle of a K-contiguous stage: physical chunk = logical chunk ^ swz_k(row)
+// (a function of row bits 0..3 only).
 __device__ __forceinline__ int swz_k(int r) {
-  return ((r ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1) | (((r >> 1) & 1) << 2);
+  if constexpr (kChunks == 8) {
+    return ((r ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1) | (((r >> 1) & 1) << 2);
+  } else {
+    return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
+  }
 }
 // Swizzle of an MN-contiguous bf16 stage: physical chunk = chunk ^ swz_mn(k-row).
 __device__ __forceinline__ int swz_mn(int k) {
@@ -120,8 +135,9 @@ struct Operand {
 // ---------------------------------------------------------------------------
 template <typename T, bool KContig> struct Side;
 
-// K-contiguous operand.  Wave w copies rows 8 (8w + i) .. +8 (i < 8): lane l
-// fills physical chunk l % 8 of row 8 (8w + i) + l / 8.
+// K-contiguous operand.  Copy i of wave w covers rows kRowsPerCopy (c w + i)
+// .. + kRowsPerCopy (c = kCopiesPerWave): lane l fills physical chunk
+// l % kChunks of row kRowsPerCopy (c w + i) + l / kChunks.
 template <typename T>
 struct Side<T, true> {
   u32x4_t rsrc;
@@ -135,13 +151,15 @@ struct Side<T, true> {
     const int64_t row_bytes = op.ld * (int64_t)sizeof(T);
     rsrc = make_rsrc(op.base + mn0 * op.ld, (op.mn_ext - mn0) * row_bytes);
     k_ext_bytes = op.k_ext * (int64_t)sizeof(T);
-    const int rsub = lane >> 3;  // 0..7: row within an 8-row copy
-    // swz_k depends on row bits 0..3: bit 3 is the parity of the copy index
+    const int rsub = lane / kChunks;  // row within a copy
+    // swz_k depends on row bits 0..3; with 8 rows per copy bit 3 is the parity
+    // of the copy index, with 16 it is fixed by the lane
 #pragma unroll
-    for (int p = 0; p < 2; ++p) kbyte[p] = (uint32_t)(((lane & 7) ^ swz_k(rsub + 8 * p)) * 16);
+    for (int p = 0; p < 2; ++p)
+      kbyte[p] = (uint32_t)(((lane % kChunks) ^ swz_k(rsub + kRowsPerCopy * p)) * 16);
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) {
-      const int row = 8 * (kCopiesPerWave * wave + i) + rsub;
+      const int row = kRowsPerCopy * (kCopiesPerWave * wave + i) + rsub;
       voff[i] = (uint32_t)(row * row_bytes) + kbyte[i & 1];
     }
     const int frow = wsub * kWaveTile + (lane & 31);
@@ -151,18 +169,19 @@ struct Side<T, true> {
       frag_off[j] = (uint32_t)(frow * kStageRowBytes + ((ch ^ swz_k(frow)) * 16));
     }
   }
-  // Copy stage kt (K bytes [kt*128, kt*128 + 128)) to LDS address dst; a dead
-  // copy (live == false) reads zeros.
-  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
-    const uint32_t soff = live ? (uint32_t)(kt * kStageRowBytes) : 0u;
+  // Copy stage kt (K bytes [kt, kt + 1) * kStageRowBytes) to LDS address dst;
+  // a dead copy (live == false) reads zeros.
+  // Copy i (< kCopiesPerWave) of this wave.
+  __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
+                                          int i) const {
     const int64_t k0 = kt * kStageRowBytes;
-    const bool ok0 = live && k0 + kbyte[0] < k_ext_bytes;
-    const bool ok1 = live && k0 + kbyte[1] < k_ext_bytes;
+    const uint32_t soff = live ? (uint32_t)k0 : 0u;
+    const bool ok = live && k0 + kbyte[i & 1] < k_ext_bytes;
+    dma16(rsrc, dst + (kCopiesPerWave * wave + i) * 1024, ok ? voff[i] : kOutOfRange, soff);
+  }
+  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) {
-      const bool ok = (i & 1) ? ok1 : ok0;
-      dma16(rsrc, dst + (kCopiesPerWave * wave + i) * 1024, ok ? voff[i] : kOutOfRange, soff);
-    }
+    for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
   }
   // Fragment of sub-tile mi for k step j of the stage at src.
   __device__ __forceinline__ u32x4_t frag(const char* src, int mi, int j) const {
@@ -170,9 +189,9 @@ struct Side<T, true> {
   }
 };
 
-// MN-contiguous bf16 operand: a stage is 64 k-rows x 256 mn.  Wave w copies
-// k-rows 2 (8w + i) and +1; lane l fills physical chunk l % 32 of k-row
-// 2 (8w + i) + l / 32.
+// MN-contiguous bf16 operand: a stage is kStageRowBytes / 2 k-rows x 256 mn.
+// Copy i of wave w covers k-rows 2 (c w + i) and +1 (c = kCopiesPerWave); lane
+// l fills physical chunk l % 32 of k-row 2 (c w + i) + l / 32.
 template <>
 struct Side<__bf16, false> {
   const char* base;       // element (mn0, k = 0)
@@ -209,14 +228,16 @@ struct Side<__bf16, false> {
       frag_off[mi] = (uint32_t)(kr * 512 + c * 16 + (col & 7) * 2);
     }
   }
-  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
-    const int64_t k0 = live ? kt * 64 : 0;
+  __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
+                                          int i) const {
+    const int64_t k0 = live ? kt * (kStageRowBytes / 2) : 0;
     // base points at column mn0: the record count stops at the operand's last byte
     const u32x4_t r = make_rsrc(base + k0 * row_bytes, (k_ext - k0) * row_bytes - mn0_bytes);
+    dma16(r, dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
+  }
+  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) {
-      dma16(r, dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
-    }
+    for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
   }
   __device__ __forceinline__ u32x4_t frag(const char* src, int mi, int j) const {
     const char* p = src + frag_off[mi] + j * 16 * 512;
@@ -228,8 +249,9 @@ struct Side<__bf16, false> {
   }
 };
 
-// MN-contiguous f32 operand: a stage is 32 k-rows of 256 floats (1 KiB), one
-// k-row per copy, no swizzle; fragments are read one float at a time.
+// MN-contiguous f32 operand: a stage is kStageRowBytes / 4 k-rows of 256
+// floats (1 KiB), one k-row per copy, no swizzle; fragments are read one float
+// at a time.
 template <>
 struct Side<float, false> {
   const char* base;
@@ -252,13 +274,15 @@ struct Side<float, false> {
     }
     frag_off = (uint32_t)((wsub * kWaveTile + (lane & 31)) * 4 + (lane >> 5) * 4 * 1024);
   }
-  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
-    const int64_t k0 = live ? kt * 32 : 0;
+  __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
+                                          int i) const {
+    const int64_t k0 = live ? kt * (kStageRowBytes / 4) : 0;
     const u32x4_t r = make_rsrc(base + k0 * row_bytes, (k_ext - k0) * row_bytes - mn0_bytes);
+    dma16(r, dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
+  }
+  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) {
-      dma16(r, dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
-    }
+    for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
   }
   // k step j covers k-rows 8 j .. 8 j + 7: lane half h takes rows 8 j + 4 h + q.
   __device__ __forceinline__ u32x4_t frag(const char* src, int mi, int j) const {
@@ -323,43 +347,74 @@ struct Frags {
 #pragma unroll
     for (int i = 0; i < 4; ++i) b[i] = sb.frag(stage + kOperandBytes, i, j);
   }
-  __device__ __forceinline__ void mma(Acc& acc) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jn = 0; jn < 4; ++jn) acc.c[i][jn] = Mfma<T>::run(a[i], b[jn], acc.c[i][jn]);
+  // Read r of 8, in the order the MFMAs first use them: a0, b0..b3, a1..a3.
+  __device__ __forceinline__ void read_one(const Side<T, AK>& sa, const Side<T, BK>& sb,
+                                           const char* stage, int j, int r) {
+    if (r == 0) a[0] = sa.frag(stage, 0, j);
+    else if (r <= 4) b[r - 1] = sb.frag(stage + kOperandBytes, r - 1, j);
+    else a[r - 4] = sa.frag(stage, r - 4, j);
   }
 };
 
-// Wait until this wave's copies of all but the newest `Ahead` stages have
-// landed and its own LDS reads are done (vmcnt(n) lgkmcnt(0), gfx9 encoding).
-template <int Ahead>
-__device__ __forceinline__ void wait_stage() {
-  constexpr int n = Ahead * 2 * kCopiesPerWave;  // A and B copies per stage per wave
-  static_assert(n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8));
+// Wait until at most N of this wave's copies are still in flight and its own
+// LDS reads are done (vmcnt(N) lgkmcnt(0), gfx9 encoding).  Copies complete in
+// issue order.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Keeps the instruction scheduler from moving anything across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Half a stage: the 16 MFMAs of one k step (fragments `use`), with the 8
+// fragment reads of the next k step (into `fill`, step j of the stage at src)
+// after the first 8 MFMAs, and, with Copy, the 4 copies of one operand (side
+// cs, stage kc, to dst) after MFMAs 1, 5, 9 and 13.  Spreading the copies keeps
+// the MFMA pipe fed while the texture unit works through them; issued in a
+// burst, they would hold every wave of the CU at once.
+template <bool Reads, bool Copy, typename T, bool AK, bool BK, typename CS>
+__device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, BK>& sb,
+                                           const Frags<T, AK, BK>& use, Frags<T, AK, BK>& fill,
+                                           const char* src, int j, const CS& cs, uint32_t dst,
+                                           int64_t kc, int wave, bool live, Acc& acc) {
+  static_assert(kCopiesPerWave == 4, "one copy per four MFMAs");
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    acc.c[t / 4][t % 4] = Mfma<T>::run(use.a[t / 4], use.b[t % 4], acc.c[t / 4][t % 4]);
+    if constexpr (Reads) {
+      if (t < 8) fill.read_one(sa, sb, src, j, t);
+    }
+    if constexpr (Copy) {
+      if ((t & 3) == 1) cs.copy_one(dst, kc, wave, live, t >> 2);
+    }
+    sched_fence();
+  }
 }
 
 // C[m0:m0+256, n0:n0+256] = sum_k A[m, k] B[n, k] over k in [0, k_len).
 //
-// Every iteration issues exactly one stage of copies, so the number of copies
-// in flight is the same in every iteration and the waits are constants: past
-// the last stage the copies are dead (they read zeros into a buffer that will
-// not be read again).  For stage kt (buffer kt % 2), with fragments of k step
-// j read one step ahead of the MFMAs that use them:
-//   steps 0..2: read step j+1, MFMAs of step j;
-//   wait for stage kt+1 and for the step-3 reads; barrier;
-//   copy stage kt+2 into buffer kt % 2 (every wave is past its last read);
-//   read step 0 of stage kt+1; MFMAs of step 3 of kt.
-// The last stage is peeled off so that the loop body has no branch: a path
-// that skipped the barrier would make the compiler wait for the step-0 reads
-// of the next stage before the step-3 MFMAs.
+// Stage kt lives in ring buffer kt % kStages and is two k steps: step 0 in
+// fragment set f0, step 1 in f1, each read one half stage ahead of its MFMAs.
+// Iteration kt:
+//   half A: MFMAs of step 0, reads of step 1, and the B copies of stage
+//           kt + kStages - 1 (into the buffer freed at the previous barrier);
+//   wait until stage kt + 1 has landed and this wave's reads are done; barrier
+//   (every wave is past its last read of buffer kt % kStages);
+//   half B: MFMAs of step 1, reads of step 0 of stage kt + 1, and the A copies
+//           of stage kt + kStages (into buffer kt % kStages).
+// Every iteration issues one stage of copies, so the waits are constants;
+// past the last stage the copies are dead (they read zeros into buffers that
+// are not read again).  The last stage is peeled off so that the loop body has
+// no branch.
 template <typename T, bool AK, bool BK>
 __device__ __forceinline__ void tile_mainloop(const Operand<T>& A, const Operand<T>& B,
                                               int64_t m0, int64_t n0, int64_t k_len, char* lds,
                                               Acc& acc) {
-  static_assert(kStages == 2 && kSteps == 4, "pipeline written for two stages of four steps");
+  static_assert(kSteps == 2 && kStages >= 3, "pipeline written for two k steps per stage");
   constexpr int64_t kStageK = kStageRowBytes / sizeof(T);
+  constexpr int kPerStage = 2 * kCopiesPerWave;  // copies per wave per stage
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -378,43 +433,37 @@ __device__ __forceinline__ void tile_mainloop(const Operand<T>& A, const Operand
   sb.init(B, n0, wave, lane, wn);
   const int64_t nk = (k_len + kStageK - 1) / kStageK;
 
+  // Stages 0 .. kStages - 2 whole, and the A copies of stage kStages - 1.
 #pragma unroll
-  for (int s = 0; s < kStages; ++s) {
+  for (int s = 0; s + 1 < kStages; ++s) {
     const uint32_t dst = lds0 + s * kStageBytes;
     sa.copy(dst, s, wave, s < nk);
     sb.copy(dst + kOperandBytes, s, wave, s < nk);
   }
-  wait_stage<kStages - 1>();
+  sa.copy(lds0 + (kStages - 1) * kStageBytes, kStages - 1, wave, kStages - 1 < nk);
+  wait_copies<(kStages - 2) * kPerStage + kCopiesPerWave>();
   block_barrier();
 
   Frags<T, AK, BK> f0, f1;
   f0.read(sa, sb, lds, 0);
+  sched_fence();
+  uint32_t buf = 0;  // ring buffer of stage kt
   for (int64_t kt = 0; kt + 1 < nk; ++kt) {
-    const int64_t buf = kt & 1;
-    const char* cur = lds + buf * kStageBytes;
-    f1.read(sa, sb, cur, 1);
-    f0.mma(acc);
-    f0.read(sa, sb, cur, 2);
-    f1.mma(acc);
-    f1.read(sa, sb, cur, 3);
-    f0.mma(acc);
-    wait_stage<0>();
+    const uint32_t prev = buf == 0 ? kStages - 1 : buf - 1;
+    const uint32_t next = buf + 1 == kStages ? 0u : buf + 1;
+    const int64_t ka = kt + kStages - 1;
+    half_stage<true, true>(sa, sb, f0, f1, lds + buf * kStageBytes, 1, sb,
+                           lds0 + prev * kStageBytes + kOperandBytes, ka, wave, ka < nk, acc);
+    wait_copies<(kStages - 2) * kPerStage>();
     block_barrier();
-    const uint32_t dst = lds0 + (uint32_t)(buf * kStageBytes);
-    sa.copy(dst, kt + 2, wave, kt + 2 < nk);
-    sb.copy(dst + kOperandBytes, kt + 2, wave, kt + 2 < nk);
-    f0.read(sa, sb, lds + (buf ^ 1) * kStageBytes, 0);
-    f1.mma(acc);
+    const int64_t kb = kt + kStages;
+    half_stage<true, true>(sa, sb, f1, f0, lds + next * kStageBytes, 0, sa,
+                           lds0 + buf * kStageBytes, kb, wave, kb < nk, acc);
+    buf = next;
   }
-  const char* last = lds + ((nk - 1) & 1) * kStageBytes;
-  f1.read(sa, sb, last, 1);
-  f0.mma(acc);
-  f0.read(sa, sb, last, 2);
-  f1.mma(acc);
-  f1.read(sa, sb, last, 3);
-  f0.mma(acc);
-  f1.mma(acc);
-  wait_stage<0>();  // no copy may still be writing LDS when the block exits
+  half_stage<true, false>(sa, sb, f0, f1, lds + buf * kStageBytes, 1, sa, 0u, 0, wave, false, acc);
+  half_stage<false, false>(sa, sb, f1, f0, lds, 0, sa, 0u, 0, wave, false, acc);
+  wait_copies<0>();  // no copy may still be writing LDS when the block exits
 }
 
 }  // namespace lce
