@@ -18,6 +18,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "lce_kernels.h"
 #include "tile_engine.h"
 
@@ -27,44 +29,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-constexpr int kXcds = 8;  // blocks are dispatched to the 8 XCDs round-robin
-
-// Tile coordinates of this block.  Tiles are ordered in groups of group_m
-// M-tiles: within a group N advances after every group_m tiles, so that
-// consecutive tiles share operand rows.  Each XCD (block b runs on XCD b % 8)
-// is given one contiguous range of that order, so the blocks resident on one
-// XCD at the same time work on neighbouring tiles and share its L2.
-__device__ __forceinline__ void tile_coords(int64_t m_tiles, int64_t n_tiles, int64_t group_m,
-                                            int64_t* m0, int64_t* n0) {
-  const int64_t total = m_tiles * n_tiles;
-  const int64_t b = blockIdx.x;
-  const int64_t x = b % kXcds, j = b / kXcds;
-  const int64_t q = total / kXcds, r = total % kXcds;
-  const int64_t t = x * q + (x < r ? x : r) + j;  // a bijection of [0, total)
-  const int64_t per_group = group_m * n_tiles;
-  const int64_t g = t / per_group;
-  const int64_t first_m = g * group_m;
-  const int64_t gm = m_tiles - first_m < group_m ? m_tiles - first_m : group_m;
-  const int64_t local = t - g * per_group;
-  *m0 = (first_m + local % gm) * kTile;
-  *n0 = (local / gm) * kTile;
-}
-
 // ---------------------------------------------------------------------------
 // Forward strip: MFMA M = vocabulary rows of the strip, N = tokens, K = H.
 // ---------------------------------------------------------------------------
+// Per token of the tile and per 128 strip rows of a wave: (max, sum of
+// exp(z - max)) to partials, and the target logit to z_target.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  int64_t m0, n0;
-  tile_coords(a.m_tiles, a.n_tiles, a.group_m, &m0, &n0);
-  Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
-  Operand<T> B{a.hidden, a.H, a.N, a.H};
-  Acc acc;
-  tile_mainloop<T, true, true>(A, B, m0, n0, a.H, lds, acc);
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, Acc& acc, int64_t m0,
+                                             int64_t n0) {
+  // lane values recomputed per tile rather than hoisted and kept live
+  const int tid = opaque((int)threadIdx.x);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t vrow0 = m0 + wm * kWaveTile;          // first strip row of this wave
   const int64_t rows_left = a.v_len - vrow0;
@@ -74,35 +50,33 @@ __global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) 
   const int64_t blk = vrow0 / kWaveTile;
   const int half = lane >> 5;
 
-  if (!full) {
-    // rows past the strip's end: -inf adds nothing to the max or the sum
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const bool out = acc_row(mi, e, lane) >= nrows;
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc.c[mi][ni][e] = out ? -INFINITY : acc.c[mi][ni][e];
-      }
-  }
-
+  // One 32-token column block (ni) at a time, so that only its 64 values per
+  // lane are held in VGPRs.
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
     const bool tok_ok = tok < a.N;
-    float mx = -INFINITY;
+    float v[64];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc.c[mi][ni][e]);
+      for (int e = 0; e < 16; ++e) v[mi * 16 + e] = acc.c[mi][ni][e];
+    if (!full) {
+      // rows past the strip's end: -inf adds nothing to the max or the sum
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          v[mi * 16 + e] = acc_row(mi, e, lane) >= nrows ? -INFINITY : v[mi * 16 + e];
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 64; ++q) mx = fmaxf(mx, v[q]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mscaled = mx * kLog2e;
     float sum = 0.f;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        sum += fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, -mscaled));
+    for (int q = 0; q < 64; ++q) sum += fast_exp2(__builtin_fmaf(v[q], kLog2e, -mscaled));
     sum += __shfl_xor(sum, 32);
     if (half == 0 && tok_ok) a.partials[blk * a.N + tok] = float2{mx, sum};
 
@@ -119,12 +93,25 @@ __global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) 
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const bool eq = hit && acc_row(mi, e, lane) == lr;
-          zt = eq ? acc.c[mi][ni][e] : zt;
+          zt = eq ? v[mi * 16 + e] : zt;
           mine = mine || eq;
         }
       if (mine) a.z_target[tok] = zt;
     }
+    sched_fence();
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
+  const Operand<T> B{a.hidden, a.H, a.N, a.H};
+  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m};
+  run_tiles<T, true, true>(A, B, a.H, grid, lds,
+                           [&](Acc& acc, int64_t m0, int64_t n0, char*) {
+                             lse_epilogue(a, acc, m0, n0);
+                           });
 }
 
 // ---------------------------------------------------------------------------
@@ -155,29 +142,22 @@ template <> struct GPack<float> {
 // thread stores whole 16-byte runs of a row, so a wave writes 512 (bf16) or
 // 1024 (f32) contiguous bytes of G per instruction.
 template <typename T> struct GradStage {
-  static constexpr int kTok = sizeof(T) == 2 ? 128 : 64;      // tokens per pass
+  static constexpr int kTok = sizeof(T) == 2 ? 64 : 32;       // tokens per pass
   static constexpr int kRowBytes = kTile * (int)sizeof(T);      // 256 vocabulary columns
   static constexpr int kStride = kRowBytes + 16;                // padded LDS row
   static constexpr int kRunsPerRow = kRowBytes / 16;
   static constexpr int kRowsPerSweep = kThreads / kRunsPerRow;
   static constexpr int kSweeps = kTok / kRowsPerSweep;
-  static_assert(kTok * kStride <= kLdsBytes, "staging fits in LDS");
+  static_assert(kTok * kStride <= kStagingBytes, "staging fits in LDS");
 };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  int64_t m0, n0;
-  tile_coords(a.m_tiles, a.n_tiles, a.group_m, &m0, &n0);
-  Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
-  Operand<T> B{a.hidden, a.H, a.N, a.H};
-  Acc acc;
-  tile_mainloop<T, true, true>(A, B, m0, n0, a.H, lds, acc);
-
+__device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, int64_t m0,
+                                              int64_t n0, char* lds) {
   typedef GradStage<T> S;
-  const int tid = threadIdx.x;
+  const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t vrow0 = m0 + wm * kWaveTile;
   const bool full = vrow0 + kWaveTile <= a.v_len;  // no strip rows past v_len in this wave
@@ -215,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
 
 #pragma unroll
   for (int pass = 0; pass < kTile / S::kTok; ++pass) {
-    block_barrier();  // LDS free: main loop reads (pass 0) or previous pass done
+    block_barrier();  // staging free: the previous pass (or tile) is done with it
     const int tok_base = pass * S::kTok;  // first token of the pass within the tile
     if (wn == tok_base / kWaveTile) {
 #pragma unroll
@@ -246,32 +226,140 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
   }
 }
 
+// bf16 strips: G for the whole tile is packed into VGPRs by all waves at
+// once (per element one FMA, one exp2 and half a pack: the token's |scale| is
+// folded into the exponent, its sign applied to the packed bits), then leaves
+// in two passes of 128 tokens through the 64 KiB staging area: 128 rows of
+// 512 bytes whose 16-byte chunks are XOR-swizzled by the row, so that neither
+// the MFMA-layout writes nor the row reads pile onto a few banks.
+__device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& acc, int64_t m0,
+                                              int64_t n0, char* lds) {
+  constexpr int kRowBytes = kTile * 2;        // 256 bf16 vocabulary columns
+  constexpr int kPassTok = 128;               // tokens per pass: one wave column
+  static_assert(kPassTok * kRowBytes <= kStagingBytes, "staging fits in LDS");
+  const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int half = lane >> 5;
+  const int64_t vrow0 = m0 + wm * kWaveTile;
+  const bool full = vrow0 + kWaveTile <= a.v_len;  // no strip rows past v_len in this wave
+  const float scale_all = a.ctrl->grad_scale;
+  const float abs_scale = fabsf(scale_all);
+  const uint32_t sign = scale_all < 0.f ? 0x80008000u : 0u;
+  const float log2_scale = __builtin_amdgcn_logf(abs_scale);  // -inf for a zero scale
+
+  u32x2_t gp[4][4][4];  // [ni][mi][q]: G of rows acc_row(mi, 4q .. 4q + 3), bf16 pairs
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
+    const bool tok_ok = tok < a.N;
+    const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
+    const bool valid = t != a.ignore_index;
+    const float lse2 = (tok_ok ? a.lse[tok] : 0.f) * kLog2e;
+    // |scale| * exp(z - lse) = exp2(z log2e + c); an ignored token gets c = -inf
+    const float c = valid ? log2_scale - lse2 : -INFINITY;
+    const int64_t tl64 = (int64_t)t - (a.v_begin + vrow0);  // target row in this wave
+    const bool hit = valid && tl64 >= 0 && tl64 < kWaveTile;
+    const int tl = hit ? (int)tl64 : -1;
+    const bool any_hit = __any(hit);
+    float v[64];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        v[mi * 16 + e] = fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, c));
+    if (!full) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          v[mi * 16 + e] = vrow0 + acc_row(mi, e, lane) < a.v_len ? v[mi * 16 + e] : 0.f;
+    }
+    if (any_hit) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          v[mi * 16 + e] = acc_row(mi, e, lane) == tl ? v[mi * 16 + e] - abs_scale : v[mi * 16 + e];
+    }
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float* w = &v[mi * 16 + 4 * q];
+        const u32x2_t p = GPack<__bf16>::pack(w[0], w[1], w[2], w[3]);
+        gp[ni][mi][q] = u32x2_t{p[0] ^ sign, p[1] ^ sign};
+      }
+    sched_fence();
+  }
+
+  // G rows n0.. of the strip buffer from column m0: byte offset
+  // (tok - n0) * ldg * 2 + (col - m0) * 2; rows past N are out of range.
+  const int64_t row_bytes = a.ldg * 2;
+  const __amdgpu_buffer_rsrc_t gbuf =
+      make_buffer(a.g_strip + n0 * a.ldg + m0, (a.N - n0) * row_bytes - m0 * 2);
+#pragma unroll
+  for (int pass = 0; pass < kTile / kPassTok; ++pass) {
+    block_barrier();  // staging free: the previous pass (or tile) is done with it
+    if (wn == pass) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int row = ni * 32 + (lane & 31);  // token within the pass
+        char* lrow = lds + row * kRowBytes + half * 8;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int chunk = wm * 16 + mi * 4 + q;  // 16-byte chunk of columns
+            *reinterpret_cast<u32x2_t*>(lrow + ((chunk ^ (row & 31)) * 16)) = gp[ni][mi][q];
+          }
+      }
+    }
+    block_barrier();
+    const int run = tid & 31;  // 16-byte run of a row
+#pragma unroll
+    for (int i = 0; i < kPassTok * 32 / kThreads; ++i) {
+      const int row = (tid >> 5) + (kThreads / 32) * i;
+      const u32x4_t val =
+          *reinterpret_cast<const u32x4_t*>(lds + row * kRowBytes + ((run ^ (row & 31)) * 16));
+      const uint32_t off = (uint32_t)((pass * kPassTok + row) * row_bytes) + run * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(val, gbuf, off, 0, 0);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
+  const Operand<T> B{a.hidden, a.H, a.N, a.H};
+  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m};
+  run_tiles<T, true, true>(A, B, a.H, grid, lds,
+                           [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
+                             grad_epilogue(a, acc, m0, n0, staging);
+                           });
+}
+
 // ---------------------------------------------------------------------------
 // Plain fp32-output GEMM tile: C[m, n] (+)= sum_k A[m, k] B[n, k].
 //
-// The epilogue goes through LDS (free once the main loop is done) in four
-// passes of 64 rows: the two waves that hold those rows write them, then all
-// 256 threads move whole 16-byte runs of each row, so that every wave reads
-// and writes 1 KiB of one row of C per instruction, and a pass issues all its
-// loads (read-modify-write for Accum) before any add.
+// The epilogue goes through the LDS staging area in eight passes of 32 rows
+// (one MFMA row block of one wave row): the two waves that hold those rows
+// write them, then all 256 threads move whole 16-byte runs of each row, so
+// that every wave reads and writes 1 KiB of one row of C per instruction, and
+// a pass issues all its loads (read-modify-write for Accum) before any add.
 // ---------------------------------------------------------------------------
-constexpr int kEpiRows = 64;                       // rows of C per pass
+constexpr int kEpiRows = 32;                       // rows of C per pass
 constexpr int kEpiStride = kTile * 4 + 16;          // padded LDS row (bytes)
-static_assert(kEpiRows * kEpiStride <= kLdsBytes, "epilogue staging fits in LDS");
+static_assert(kEpiRows * kEpiStride <= kStagingBytes, "epilogue staging fits in LDS");
 
-template <typename T, bool AK, bool BK, bool Accum>
-__global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  int64_t m0, n0;
-  tile_coords(g.m_tiles, g.n_tiles, g.group_m, &m0, &n0);
-  Operand<T> A{g.a, g.lda, g.a_mn_ext, g.a_k_ext};
-  Operand<T> B{g.b, g.ldb, g.b_mn_ext, g.b_k_ext};
-  Acc acc;
-  tile_mainloop<T, AK, BK>(A, B, m0, n0, g.k_len, lds, acc);
-
-  const int tid = threadIdx.x;
+template <typename T, bool Accum>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs<T>& g, Acc& acc, int64_t m0,
+                                              int64_t n0, char* lds) {
+  const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   // C from (m0, n0): byte offset (row - m0) * ldc * 4 + (col - n0) * 4.  Rows
   // past m fall past the record count; 16-byte runs past n get an
@@ -285,20 +373,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g)
 
 #pragma unroll
   for (int pass = 0; pass < kTile / kEpiRows; ++pass) {
-    block_barrier();  // LDS free: main loop reads (pass 0) or previous pass done
-    if (wm == pass / 2) {
-      // rows (pass % 2) * 64 .. +64 of this wave's 128 = sub-tiles mi = 2 (pass % 2) + {0, 1}
+    block_barrier();  // staging free: the previous pass (or tile) is done with it
+    if (wm == pass / 4) {
+      // rows 32 (pass % 4) .. +32 of this wave's 128 = sub-tile mi = pass % 4
+      const int mi = pass % 4;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int mi = 2 * (pass % 2) + h;
+      for (int ni = 0; ni < 4; ++ni) {
+        const int col = wn * kWaveTile + ni * 32 + (lane & 31);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int col = wn * kWaveTile + ni * 32 + (lane & 31);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int row = h * 32 + acc_row(0, e, lane);
-            *reinterpret_cast<float*>(lds + row * kEpiStride + col * 4) = acc.c[mi][ni][e];
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int row = acc_row(0, e, lane);
+          *reinterpret_cast<float*>(lds + row * kEpiStride + col * 4) = acc.c[mi][ni][e];
         }
       }
     }
@@ -326,6 +411,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v[i]), cbuf, off, 0, 0);
     }
   }
+}
+
+template <typename T, bool AK, bool BK, bool Accum>
+__global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const Operand<T> A{g.a, g.lda, g.a_mn_ext, g.a_k_ext};
+  const Operand<T> B{g.b, g.ldb, g.b_mn_ext, g.b_k_ext};
+  const TileGrid grid{g.m_tiles, g.n_tiles, g.group_m};
+  run_tiles<T, AK, BK>(A, B, g.k_len, grid, lds,
+                       [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
+                         gemm_epilogue<T, Accum>(g, acc, m0, n0, staging);
+                       });
 }
 
 // ---------------------------------------------------------------------------
@@ -435,12 +532,46 @@ constexpr int64_t kStripGroupM = 8;
 // Output GEMMs: 4 M-tiles per group, all N-tiles of those rows.
 constexpr int64_t kGemmGroupM = 4;
 
+// Compute units of the current device, rounded down to a multiple of the XCD
+// count (queried once per device).
+static int64_t persistent_blocks() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>* slot = dev < 64 ? &cache[dev] : nullptr;
+  int n = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = kXcds;
+    n = n / kXcds * kXcds;
+    if (n <= 0) n = kXcds;
+    if (slot) slot->store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Blocks for `tiles` tiles of `nk` stages each: one per compute unit, each
+// looping over its tiles, when a tile has more stages than the ring holds
+// (so the copy stream is never more than one tile ahead); else one per tile.
+static int64_t grid_blocks(int64_t tiles, int64_t nk) {
+  if (nk <= kStages) return tiles;
+  const int64_t p = persistent_blocks();
+  return tiles < p ? tiles : p;
+}
+
+template <typename T>
+static int64_t stages_of(int64_t k_len) {
+  constexpr int64_t kStageK = kStageRowBytes / sizeof(T);
+  return (k_len + kStageK - 1) / kStageK;
+}
+
 template <typename T>
 hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st) {
   a.m_tiles = cdiv(a.v_len, kTile);
   a.n_tiles = cdiv(a.N, kTile);
   a.group_m = kStripGroupM;
-  const int64_t blocks = a.m_tiles * a.n_tiles;
+  const int64_t blocks = grid_blocks(a.m_tiles * a.n_tiles, stages_of<T>(a.H));
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_lse_kernel<T>));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(strip_lse_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, st, a);
@@ -452,7 +583,7 @@ hipError_t launch_strip_grad(StripArgs<T> a, hipStream_t st) {
   a.m_tiles = cdiv(a.v_len, kTile);
   a.n_tiles = cdiv(a.N, kTile);
   a.group_m = kStripGroupM;
-  const int64_t blocks = a.m_tiles * a.n_tiles;
+  const int64_t blocks = grid_blocks(a.m_tiles * a.n_tiles, stages_of<T>(a.H));
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_grad_kernel<T>));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(strip_grad_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, st, a);
@@ -464,7 +595,7 @@ static hipError_t launch_gemm(GemmArgs<T> g, hipStream_t st) {
   g.m_tiles = cdiv(g.m, kTile);
   g.n_tiles = cdiv(g.n, kTile);
   g.group_m = kGemmGroupM;
-  const int64_t blocks = g.m_tiles * g.n_tiles;
+  const int64_t blocks = grid_blocks(g.m_tiles * g.n_tiles, stages_of<T>(g.k_len));
   hipError_t e =
       set_lds<T>(reinterpret_cast<const void*>(&gemm_f32out_kernel<T, AK, BK, Accum>));
   if (e != hipSuccess) return e;

@@ -50,13 +50,15 @@ constexpr int kSteps = kStageRowBytes / 32;   // k16 (bf16) / k8 (f32) steps per
 constexpr int kChunks = kStageRowBytes / 16;  // 16-byte chunks per row per stage
 constexpr int kOperandBytes = kTile * kStageRowBytes;   // per operand per stage
 constexpr int kStageBytes = 2 * kOperandBytes;          // A and B
-constexpr int kStages = 4;                 // ring of stages in LDS
-constexpr int kLdsBytes = kStages * kStageBytes;
+constexpr int kStages = 3;                 // ring of stages in LDS
+constexpr int kRingBytes = kStages * kStageBytes;
+constexpr int kStagingBytes = 64 * 1024;   // epilogue staging, after the ring
+constexpr int kLdsBytes = kRingBytes + kStagingBytes;
 constexpr int kCopiesPerWave = kOperandBytes / 1024 / 4;  // 1 KiB per wave-wide copy
 constexpr int kRowsPerCopy = 1024 / kStageRowBytes;       // K-contiguous rows per copy
 static_assert(kStageRowBytes == 64 || kStageRowBytes == 128, "stage of 64 or 128 bytes per row");
 static_assert(kSteps % 2 == 0, "fragments alternate between two register sets");
-static_assert(kStages >= 2 && kLdsBytes <= 160 * 1024, "ring fits in LDS");
+static_assert(kStages >= 3 && kLdsBytes <= 160 * 1024, "ring and staging fit in LDS");
 constexpr uint32_t kOutOfRange = 0x80000000u;           // voffset that reads zeros
 constexpr int kRsrcWord3 = 0x00020000;                  // raw buffer, gfx9 family
 
@@ -146,10 +148,13 @@ struct Side<T, true> {
   int64_t k_ext_bytes;
   uint32_t frag_off[kSteps];  // per k step: byte offset of this lane's fragment (mi = 0)
 
-  __device__ __forceinline__ void init(const Operand<T>& op, int64_t mn0, int wave, int lane,
-                                       int wsub) {
+  // Point the copies at the tile whose first row is mn0.
+  __device__ __forceinline__ void retarget(const Operand<T>& op, int64_t mn0) {
+    rsrc = make_rsrc(op.base + mn0 * op.ld, (op.mn_ext - mn0) * op.ld * (int64_t)sizeof(T));
+  }
+  // Per-lane copy and fragment offsets (the same for every tile).
+  __device__ __forceinline__ void init_lanes(const Operand<T>& op, int wave, int lane, int wsub) {
     const int64_t row_bytes = op.ld * (int64_t)sizeof(T);
-    rsrc = make_rsrc(op.base + mn0 * op.ld, (op.mn_ext - mn0) * row_bytes);
     k_ext_bytes = op.k_ext * (int64_t)sizeof(T);
     const int rsub = lane / kChunks;  // row within a copy
     // swz_k depends on row bits 0..3; with 8 rows per copy bit 3 is the parity
@@ -168,6 +173,11 @@ struct Side<T, true> {
       const int ch = 2 * j + (lane >> 5);
       frag_off[j] = (uint32_t)(frow * kStageRowBytes + ((ch ^ swz_k(frow)) * 16));
     }
+  }
+  __device__ __forceinline__ void init(const Operand<T>& op, int64_t mn0, int wave, int lane,
+                                       int wsub) {
+    init_lanes(op, wave, lane, wsub);
+    retarget(op, mn0);
   }
   // Copy stage kt (K bytes [kt, kt + 1) * kStageRowBytes) to LDS address dst;
   // a dead copy (live == false) reads zeros.
@@ -201,12 +211,19 @@ struct Side<__bf16, false> {
   uint32_t voff[kCopiesPerWave];
   uint32_t frag_off[4];   // per mi: byte offset of this lane's first transposed read
 
+  __device__ __forceinline__ void retarget(const Operand<__bf16>& op, int64_t mn0) {
+    base = reinterpret_cast<const char*>(op.base + mn0);
+    mn0_bytes = mn0 * 2;
+  }
   __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane,
                                        int wsub) {
+    init_lanes(op, wave, lane, wsub);
+    retarget(op, mn0);
+  }
+  __device__ __forceinline__ void init_lanes(const Operand<__bf16>& op, int wave, int lane,
+                                             int wsub) {
     row_bytes = op.ld * 2;
-    base = reinterpret_cast<const char*>(op.base + mn0);
     k_ext = op.k_ext;
-    mn0_bytes = mn0 * 2;
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) {
       const int kr = 2 * (kCopiesPerWave * wave + i) + (lane >> 5);
@@ -261,12 +278,19 @@ struct Side<float, false> {
   uint32_t voff[kCopiesPerWave];
   uint32_t frag_off;
 
+  __device__ __forceinline__ void retarget(const Operand<float>& op, int64_t mn0) {
+    base = reinterpret_cast<const char*>(op.base + mn0);
+    mn0_bytes = mn0 * 4;
+  }
   __device__ __forceinline__ void init(const Operand<float>& op, int64_t mn0, int wave, int lane,
                                        int wsub) {
+    init_lanes(op, wave, lane, wsub);
+    retarget(op, mn0);
+  }
+  __device__ __forceinline__ void init_lanes(const Operand<float>& op, int wave, int lane,
+                                             int wsub) {
     row_bytes = op.ld * 4;
-    base = reinterpret_cast<const char*>(op.base + mn0);
     k_ext = op.k_ext;
-    mn0_bytes = mn0 * 4;
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) {
       const int kr = kCopiesPerWave * wave + i;
@@ -365,6 +389,13 @@ __device__ __forceinline__ void wait_copies() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
+// x, hidden from the optimiser: values computed from it are recomputed where
+// they are written instead of being hoisted and kept live.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Keeps the instruction scheduler from moving anything across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
@@ -393,26 +424,129 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
   }
 }
 
-// C[m0:m0+256, n0:n0+256] = sum_k A[m, k] B[n, k] over k in [0, k_len).
+// ---------------------------------------------------------------------------
+// Tile order and the persistent tile loop.
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;  // blocks are dispatched to the 8 XCDs round-robin
+
+// Tiles of an M x N output, ordered in groups of group_m M-tiles: within a
+// group N advances after every group_m tiles, so that consecutive tiles share
+// operand rows.  Each XCD (block b runs on XCD b % 8) is given one contiguous
+// range of that order, so the tiles resident on one XCD at the same time are
+// neighbours and share its L2.  Block b takes the tiles of virtual blocks
+// b, b + G, b + 2G, ... (G blocks; G is the tile count or a multiple of 8, so
+// that every virtual block of b maps to b's XCD).
+struct TileGrid {
+  int64_t m_tiles, n_tiles, group_m;
+
+  __device__ __forceinline__ int64_t total() const { return m_tiles * n_tiles; }
+  // Tiles taken by this block.
+  __device__ __forceinline__ int64_t count() const {
+    const int64_t g = gridDim.x;
+    return (total() - blockIdx.x + g - 1) / g;
+  }
+  // First row and column of this block's i-th tile.
+  __device__ __forceinline__ void coords(int64_t i, int64_t* m0, int64_t* n0) const {
+    const int64_t b = blockIdx.x + i * (int64_t)gridDim.x;
+    const int64_t x = b % kXcds, j = b / kXcds;
+    const int64_t q = total() / kXcds, r = total() % kXcds;
+    const int64_t t = x * q + (x < r ? x : r) + j;  // a bijection of [0, total)
+    const int64_t per_group = group_m * n_tiles;
+    const int64_t g = t / per_group;
+    const int64_t first_m = g * group_m;
+    const int64_t gm = m_tiles - first_m < group_m ? m_tiles - first_m : group_m;
+    const int64_t local = t - g * per_group;
+    *m0 = (first_m + local % gm) * kTile;
+    *n0 = (local / gm) * kTile;
+  }
+};
+
+// Copies of one operand for a stream of stages that runs across this block's
+// tiles: the stage `kt` of tile `ti`, in ring buffer `buf`.
+template <typename T, bool KC>
+struct Cursor {
+  Side<T, KC> side;
+  int64_t kt, ti;
+  uint32_t buf;
+  // Copy i of the current stage (the operand's half of the ring buffer at off).
+  __device__ __forceinline__ void copy_one(uint32_t lds0, uint32_t off, int wave, int64_t tiles,
+                                           int i) const {
+    side.copy_one(lds0 + buf * kStageBytes + off, kt, wave, ti < tiles, i);
+  }
+  __device__ __forceinline__ void copy(uint32_t lds0, uint32_t off, int wave, int64_t tiles) const {
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) copy_one(lds0, off, wave, tiles, i);
+  }
+  // On to the next stage; the stream enters the next tile (first row next_mn0)
+  // after the last stage of a tile.
+  __device__ __forceinline__ void advance(const Operand<T>& op, int64_t nk, int64_t next_mn0) {
+    buf = buf + 1 == kStages ? 0u : buf + 1;
+    if (++kt == nk) {
+      kt = 0;
+      ++ti;
+      side.retarget(op, next_mn0);
+    }
+  }
+};
+
+// Half a stage: the 16 MFMAs of one k step (fragments `use`), with the 8
+// fragment reads of the next k step (into `fill`, step j of the stage at src)
+// after the first 8 MFMAs, and, with Copy, the 4 copies of one operand's
+// current stage after MFMAs 1, 5, 9 and 13.  Spreading the copies keeps the
+// MFMA pipe fed while the texture unit works through them; issued in a burst,
+// they would hold every wave of the CU at once.
+template <bool Reads, bool Copy, typename T, bool AK, bool BK, typename C>
+__device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, BK>& sb,
+                                           const Frags<T, AK, BK>& use, Frags<T, AK, BK>& fill,
+                                           const char* src, int j, const C& cur, uint32_t lds0,
+                                           uint32_t off, int wave, int64_t tiles, Acc& acc) {
+  static_assert(kCopiesPerWave == 4, "one copy per four MFMAs");
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    acc.c[t / 4][t % 4] = Mfma<T>::run(use.a[t / 4], use.b[t % 4], acc.c[t / 4][t % 4]);
+    if constexpr (Reads) {
+      if (t < 8) fill.read_one(sa, sb, src, j, t);
+    }
+    if constexpr (Copy) {
+      if ((t & 3) == 1) cur.copy_one(lds0, off, wave, tiles, t >> 2);
+    }
+    sched_fence();
+  }
+}
+
+// Every tile of this block: C[m0:m0+256, n0:n0+256] = sum_k A[m, k] B[n, k]
+// over k in [0, k_len), then epi(acc, m0, n0, staging) with the tile in acc
+// and kStagingBytes of LDS after the ring free for the epilogue.
 //
-// Stage kt lives in ring buffer kt % kStages and is two k steps: step 0 in
-// fragment set f0, step 1 in f1, each read one half stage ahead of its MFMAs.
-// Iteration kt:
-//   half A: MFMAs of step 0, reads of step 1, and the B copies of stage
-//           kt + kStages - 1 (into the buffer freed at the previous barrier);
-//   wait until stage kt + 1 has landed and this wave's reads are done; barrier
-//   (every wave is past its last read of buffer kt % kStages);
-//   half B: MFMAs of step 1, reads of step 0 of stage kt + 1, and the A copies
-//           of stage kt + kStages (into buffer kt % kStages).
-// Every iteration issues one stage of copies, so the waits are constants;
-// past the last stage the copies are dead (they read zeros into buffers that
-// are not read again).  The last stage is peeled off so that the loop body has
-// no branch.
-template <typename T, bool AK, bool BK>
-__device__ __forceinline__ void tile_mainloop(const Operand<T>& A, const Operand<T>& B,
-                                              int64_t m0, int64_t n0, int64_t k_len, char* lds,
-                                              Acc& acc) {
-  static_assert(kSteps == 2 && kStages >= 3, "pipeline written for two k steps per stage");
+// All tiles of the block form one stream of stages (a tile is nk stages of
+// two k steps; stage s lives in ring buffer s % kStages).  The copies run
+// ahead of the MFMAs by the depth of the ring, across tile boundaries, so the
+// first stages of the next tile land while a tile's epilogue runs.  With the
+// MFMAs at stage s (step 0 in fragment set f0, step 1 in f1):
+//   half A: MFMAs of step 0, reads of step 1, B copies of stage s + kStages - 1
+//           (into the buffer freed at the previous barrier);
+//   wait until stage s + 1 has landed and this wave's reads are done; barrier
+//           (every wave is past its last read of buffer s % kStages);
+//   half B: MFMAs of step 1, reads of step 0 of stage s + 1, A copies of stage
+//           s + kStages (into buffer s % kStages).
+// Every stage issues one stage of copies, so the waits are constants; past the
+// block's last stage the copies are dead (they read zeros into buffers that
+// are not read again).  The last stage of a tile is peeled off, so the loop
+// body has no branch.  A cursor enters the next tile while the MFMAs are
+// still in this one if nk > kStages; with fewer stages per tile, launch one
+// tile per block (the copies past it are dead).
+//
+// The epilogue's stores (and loads) share vmcnt with the copies.  A counted
+// wait vmcnt(n), n = copies issued after the awaited ones, stays exact: loads
+// complete in issue order among themselves, so while an awaited copy is
+// outstanding so is every later copy, and the count cannot drop to n;
+// uncounted later loads only make the wait stricter, and stores, which may
+// complete in any order relative to loads, are not counted at all.  So the
+// epilogue's stores drain behind the next tile's MFMAs.
+template <typename T, bool AK, bool BK, typename Epi>
+__device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int64_t k_len,
+                                          const TileGrid& grid, char* lds, Epi&& epi) {
+  static_assert(kSteps == 2, "pipeline written for two k steps per stage");
   constexpr int64_t kStageK = kStageRowBytes / sizeof(T);
   constexpr int kPerStage = 2 * kCopiesPerWave;  // copies per wave per stage
   const int tid = threadIdx.x;
@@ -421,48 +555,80 @@ __device__ __forceinline__ void tile_mainloop(const Operand<T>& A, const Operand
   const int wm = wave & 1;
   const int wn = wave >> 1;
   const uint32_t lds0 = lds_addr(lds);
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc.c[i][j] = f32x16_t{};
-
-  Side<T, AK> sa;
-  Side<T, BK> sb;
-  sa.init(A, m0, wave, lane, wm);
-  sb.init(B, n0, wave, lane, wn);
+  char* const staging = lds + kRingBytes;
   const int64_t nk = (k_len + kStageK - 1) / kStageK;
+  const int64_t tiles = grid.count();
+
+  int64_t m0, n0, next_m0, next_n0;  // this tile, and the next one
+  grid.coords(0, &m0, &n0);
+  next_m0 = m0;
+  next_n0 = n0;
+  if (tiles > 1) grid.coords(1, &next_m0, &next_n0);
+
+  Cursor<T, AK> ca{{}, 0, 0, 0u};
+  Cursor<T, BK> cb{{}, 0, 0, 0u};
+  ca.side.init(A, m0, wave, lane, wm);
+  cb.side.init(B, n0, wave, lane, wn);
+  const Side<T, AK>& sa = ca.side;  // fragment offsets do not depend on the tile
+  const Side<T, BK>& sb = cb.side;
 
   // Stages 0 .. kStages - 2 whole, and the A copies of stage kStages - 1.
 #pragma unroll
   for (int s = 0; s + 1 < kStages; ++s) {
-    const uint32_t dst = lds0 + s * kStageBytes;
-    sa.copy(dst, s, wave, s < nk);
-    sb.copy(dst + kOperandBytes, s, wave, s < nk);
+    ca.copy(lds0, 0, wave, tiles);
+    ca.advance(A, nk, next_m0);
+    cb.copy(lds0, kOperandBytes, wave, tiles);
+    cb.advance(B, nk, next_n0);
   }
-  sa.copy(lds0 + (kStages - 1) * kStageBytes, kStages - 1, wave, kStages - 1 < nk);
+  ca.copy(lds0, 0, wave, tiles);
+  ca.advance(A, nk, next_m0);
   wait_copies<(kStages - 2) * kPerStage + kCopiesPerWave>();
   block_barrier();
 
+  Acc acc;
   Frags<T, AK, BK> f0, f1;
-  f0.read(sa, sb, lds, 0);
-  sched_fence();
-  uint32_t buf = 0;  // ring buffer of stage kt
-  for (int64_t kt = 0; kt + 1 < nk; ++kt) {
-    const uint32_t prev = buf == 0 ? kStages - 1 : buf - 1;
-    const uint32_t next = buf + 1 == kStages ? 0u : buf + 1;
-    const int64_t ka = kt + kStages - 1;
-    half_stage<true, true>(sa, sb, f0, f1, lds + buf * kStageBytes, 1, sb,
-                           lds0 + prev * kStageBytes + kOperandBytes, ka, wave, ka < nk, acc);
-    wait_copies<(kStages - 2) * kPerStage>();
-    block_barrier();
-    const int64_t kb = kt + kStages;
-    half_stage<true, true>(sa, sb, f1, f0, lds + next * kStageBytes, 0, sa,
-                           lds0 + buf * kStageBytes, kb, wave, kb < nk, acc);
-    buf = next;
+  uint32_t buf = 0;  // ring buffer of the stage the MFMAs are at
+  for (int64_t i = 0; i < tiles; ++i) {
+    {
+      // per-lane offsets again, so that none of them is live across an epilogue
+      const int l = opaque(lane);
+      ca.side.init_lanes(A, wave, l, wm);
+      cb.side.init_lanes(B, wave, l, wn);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc.c[r][c] = f32x16_t{};
+    f0.read(sa, sb, lds + buf * kStageBytes, 0);
+    sched_fence();
+    for (int64_t kt = 0; kt + 1 < nk; ++kt) {
+      const uint32_t next = buf + 1 == kStages ? 0u : buf + 1;
+      half_stage<true, true>(sa, sb, f0, f1, lds + buf * kStageBytes, 1, cb, lds0,
+                             kOperandBytes, wave, tiles, acc);
+      cb.advance(B, nk, next_n0);
+      wait_copies<(kStages - 2) * kPerStage>();
+      block_barrier();
+      half_stage<true, true>(sa, sb, f1, f0, lds + next * kStageBytes, 0, ca, lds0, 0, wave,
+                             tiles, acc);
+      ca.advance(A, nk, next_m0);
+      buf = next;
+    }
+    {
+      const uint32_t next = buf + 1 == kStages ? 0u : buf + 1;
+      half_stage<true, true>(sa, sb, f0, f1, lds + buf * kStageBytes, 1, cb, lds0,
+                             kOperandBytes, wave, tiles, acc);
+      cb.advance(B, nk, next_n0);
+      wait_copies<(kStages - 2) * kPerStage>();
+      block_barrier();
+      half_stage<false, true>(sa, sb, f1, f0, lds, 0, ca, lds0, 0, wave, tiles, acc);
+      ca.advance(A, nk, next_m0);
+      buf = next;
+    }
+    epi(acc, m0, n0, staging);
+    m0 = next_m0;
+    n0 = next_n0;
+    if (i + 2 < tiles) grid.coords(i + 2, &next_m0, &next_n0);
   }
-  half_stage<true, false>(sa, sb, f0, f1, lds + buf * kStageBytes, 1, sa, 0u, 0, wave, false, acc);
-  half_stage<false, false>(sa, sb, f1, f0, lds, 0, sa, 0u, 0, wave, false, acc);
   wait_copies<0>();  // no copy may still be writing LDS when the block exits
 }
 
