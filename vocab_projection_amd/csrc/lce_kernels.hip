@@ -344,15 +344,22 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
 // ---------------------------------------------------------------------------
 // Plain fp32-output GEMM tile: C[m, n] (+)= sum_k A[m, k] B[n, k].
 //
-// The epilogue goes through the LDS staging area in eight passes of 32 rows
-// (one MFMA row block of one wave row): the two waves that hold those rows
-// write them, then all 256 threads move whole 16-byte runs of each row, so
-// that every wave reads and writes 1 KiB of one row of C per instruction, and
-// a pass issues all its loads (read-modify-write for Accum) before any add.
+// The epilogue goes through the LDS staging area in four passes of 64 rows
+// (1 KiB each, unpadded: the 16-byte chunk index is XOR-swizzled by the row,
+// so the two rows of an MFMA-layout write never share banks): the two waves
+// that hold those rows write them, then all 256 threads move whole 16-byte
+// runs of each row, so that every wave reads and writes 1 KiB of one row of
+// C per instruction.  With Accum a pass issues half of its loads of C before
+// the staging writes, so that their latency hides behind them.
 // ---------------------------------------------------------------------------
-constexpr int kEpiRows = 32;                       // rows of C per pass
-constexpr int kEpiStride = kTile * 4 + 16;          // padded LDS row (bytes)
-static_assert(kEpiRows * kEpiStride <= kStagingBytes, "epilogue staging fits in LDS");
+constexpr int kEpiRows = 64;                        // rows of C per pass
+constexpr int kEpiRowBytes = kTile * 4;             // one row of C in LDS
+static_assert(kEpiRows * kEpiRowBytes <= kStagingBytes, "epilogue staging fits in LDS");
+
+// Byte offset in the staging area of 16-byte chunk `chunk` of row `row`.
+__device__ __forceinline__ int epi_offset(int row, int chunk) {
+  return row * kEpiRowBytes + ((chunk ^ (((row >> 2) & 1) << 3)) * 16);
+}
 
 template <typename T, bool Accum>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs<T>& g, Acc& acc, int64_t m0,
@@ -373,17 +380,32 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs<T>& g, Acc& acc, in
 
 #pragma unroll
   for (int pass = 0; pass < kTile / kEpiRows; ++pass) {
+    const int row0 = pass * kEpiRows;
+    // rows of this thread: row0 + wave + 4 i; byte offsets from the tile's row 0
+    const uint32_t off0 = run_ok ? (uint32_t)(row0 + wave) * ldc4 + run * 16 : kOutOfRange;
+    const uint32_t step = run_ok ? 4 * ldc4 : 0u;
+    constexpr int kEarly = kRowsPerThread / 2;  // C rows loaded before the staging writes
+    u32x4_t old[kRowsPerThread];
+    if constexpr (Accum) {
+#pragma unroll
+      for (int i = 0; i < kEarly; ++i)
+        old[i] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, off0 + i * step, 0, 0);
+    }
     block_barrier();  // staging free: the previous pass (or tile) is done with it
-    if (wm == pass / 4) {
-      // rows 32 (pass % 4) .. +32 of this wave's 128 = sub-tile mi = pass % 4
-      const int mi = pass % 4;
+    if (wm == pass / 2) {
+      // rows 64 (pass % 2) .. +64 of this wave's 128 = sub-tiles mi = 2 (pass % 2) + {0, 1}
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int col = wn * kWaveTile + ni * 32 + (lane & 31);
+      for (int h = 0; h < 2; ++h) {
+        const int mi = 2 * (pass % 2) + h;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = acc_row(0, e, lane);
-          *reinterpret_cast<float*>(lds + row * kEpiStride + col * 4) = acc.c[mi][ni][e];
+        for (int ni = 0; ni < 4; ++ni) {
+          const int col = wn * kWaveTile + ni * 32 + (lane & 31);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = h * 32 + acc_row(0, e, lane);
+            *reinterpret_cast<float*>(lds + epi_offset(row, col >> 2) + (col & 3) * 4) =
+                acc.c[mi][ni][e];
+          }
         }
       }
     }
@@ -392,24 +414,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs<T>& g, Acc& acc, in
 #pragma unroll
     for (int i = 0; i < kRowsPerThread; ++i) {
       const int row = wave + 4 * i;
-      v[i] = *reinterpret_cast<const f32x4_t*>(lds + row * kEpiStride + run * 16);
+      v[i] = *reinterpret_cast<const f32x4_t*>(lds + epi_offset(row, run));
     }
-    const int row0 = pass * kEpiRows;
-    if (Accum) {
-      u32x4_t old[kRowsPerThread];
+    if constexpr (Accum) {
 #pragma unroll
-      for (int i = 0; i < kRowsPerThread; ++i) {
-        const uint32_t off = run_ok ? (uint32_t)(row0 + wave + 4 * i) * ldc4 + run * 16 : kOutOfRange;
-        old[i] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, off, 0, 0);
-      }
+      for (int i = kEarly; i < kRowsPerThread; ++i)
+        old[i] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, off0 + i * step, 0, 0);
 #pragma unroll
       for (int i = 0; i < kRowsPerThread; ++i) v[i] += __builtin_bit_cast(f32x4_t, old[i]);
     }
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-      const uint32_t off = run_ok ? (uint32_t)(row0 + wave + 4 * i) * ldc4 + run * 16 : kOutOfRange;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v[i]), cbuf, off, 0, 0);
-    }
+    for (int i = 0; i < kRowsPerThread; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v[i]), cbuf, off0 + i * step,
+                                             0, 0);
+    sched_fence();  // one pass at a time: keeps the live registers to one pass's rows
   }
 }
 
