@@ -126,6 +126,11 @@ SMALL = [
     S.small("f32_ragged", 300, 132, 777, 256, "f32", weight_std=0.2, ignore_frac=0.05),
     S.small("bf16_one_strip", 333, 96, 700, 700),
     S.small("bf16_tiny_strip", 64, 32, 50, 8),
+    # more tiles than compute units, in uneven shares: blocks loop over several
+    # tiles and the copy stream crosses tile boundaries (strip kernels 628 and
+    # 314 tiles, dH 471; ragged K of 17 stages)
+    S.small("bf16_multi_tile", 40123, 520, 1300, 1024, ignore_frac=0.05),
+    S.small("f32_multi_tile", 20005, 136, 1100, 1024, "f32", weight_std=0.2, ignore_frac=0.05),
 ]
 
 
