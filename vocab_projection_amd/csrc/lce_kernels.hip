@@ -42,19 +42,19 @@ __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, Acc& acc, in
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int64_t vrow0 = m0 + wm * kWaveTile;          // first strip row of this wave
+  const int64_t vrow0 = m0 + wm * kWaveM;             // first strip row of this wave
   const int64_t rows_left = a.v_len - vrow0;
   if (rows_left <= 0) return;                          // wave-uniform
-  const int nrows = rows_left < kWaveTile ? (int)rows_left : kWaveTile;
-  const bool full = nrows == kWaveTile;
-  const int64_t blk = vrow0 / kWaveTile;
+  const int nrows = rows_left < kWaveM ? (int)rows_left : kWaveM;
+  const bool full = nrows == kWaveM;
+  const int64_t blk = vrow0 / kWaveM;
   const int half = lane >> 5;
 
   // One 32-token column block (ni) at a time, so that only its 64 values per
   // lane are held in VGPRs.
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < kNI; ++ni) {
+    const int64_t tok = n0 + wn * kWaveN + ni * 32 + (lane & 31);
     const bool tok_ok = tok < a.N;
     float v[64];
 #pragma unroll
@@ -159,26 +159,27 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int64_t vrow0 = m0 + wm * kWaveTile;
-  const bool full = vrow0 + kWaveTile <= a.v_len;  // no strip rows past v_len in this wave
+  const int64_t vrow0 = m0 + wm * kWaveM;
+  const bool full = vrow0 + kWaveM <= a.v_len;  // no strip rows past v_len in this wave
   const float scale_all = a.ctrl->grad_scale;
   // G rows n0.. of the strip buffer from column m0: byte offset
   // (tok - n0) * ldg * elt + (col - m0) * elt; rows past N are out of range.
   const int64_t row_bytes = a.ldg * (int64_t)sizeof(T);
   const __amdgpu_buffer_rsrc_t gbuf = make_buffer(
       a.g_strip + n0 * a.ldg + m0, (a.N - n0) * row_bytes - m0 * (int64_t)sizeof(T));
-  constexpr int kNiPerPass = S::kTok / 32 > 4 ? 4 : S::kTok / 32;
+  static_assert(S::kTok <= kWaveN && kWaveN % S::kTok == 0, "a pass lies in one wave column");
+  constexpr int kNiPerPass = S::kTok / 32;
 
   // G for every element, in place (all waves at once).
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < kNI; ++ni) {
+    const int64_t tok = n0 + wn * kWaveN + ni * 32 + (lane & 31);
     const bool tok_ok = tok < a.N;
     const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
     const float sc = t != a.ignore_index ? scale_all : 0.f;
     const float lse2 = (tok_ok ? a.lse[tok] : 0.f) * kLog2e;
     const int64_t tl64 = (int64_t)t - (a.v_begin + vrow0);  // target row in this wave
-    const bool hit = t != a.ignore_index && tl64 >= 0 && tl64 < kWaveTile;
+    const bool hit = t != a.ignore_index && tl64 >= 0 && tl64 < kWaveM;
     const int tl = hit ? (int)tl64 : -1;
     const bool any_hit = __any(hit);
 #pragma unroll
@@ -197,13 +198,13 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
   for (int pass = 0; pass < kTile / S::kTok; ++pass) {
     block_barrier();  // staging free: the previous pass (or tile) is done with it
     const int tok_base = pass * S::kTok;  // first token of the pass within the tile
-    if (wn == tok_base / kWaveTile) {
+    if (wn == tok_base / kWaveN) {
 #pragma unroll
       for (int nj = 0; nj < kNiPerPass; ++nj) {
-        const int ni = (tok_base % kWaveTile) / 32 + nj;
-        const int tok_local = wn * kWaveTile + ni * 32 + (lane & 31);
+        const int ni = (tok_base % kWaveN) / 32 + nj;
+        const int tok_local = wn * kWaveN + ni * 32 + (lane & 31);
         char* lrow = lds + (tok_local - tok_base) * S::kStride +
-                     (wm * kWaveTile + (lane >> 5) * 4) * (int)sizeof(T);
+                     (wm * kWaveM + (lane >> 5) * 4) * (int)sizeof(T);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -235,24 +236,25 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
 __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& acc, int64_t m0,
                                               int64_t n0, char* lds) {
   constexpr int kRowBytes = kTile * 2;        // 256 bf16 vocabulary columns
-  constexpr int kPassTok = 128;               // tokens per pass: one wave column
+  constexpr int kPassTok = 128;               // tokens per pass
+  static_assert(kPassTok % kWaveN == 0, "a pass holds whole wave columns");
   static_assert(kPassTok * kRowBytes <= kStagingBytes, "staging fits in LDS");
   const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int half = lane >> 5;
-  const int64_t vrow0 = m0 + wm * kWaveTile;
-  const bool full = vrow0 + kWaveTile <= a.v_len;  // no strip rows past v_len in this wave
+  const int64_t vrow0 = m0 + wm * kWaveM;
+  const bool full = vrow0 + kWaveM <= a.v_len;  // no strip rows past v_len in this wave
   const float scale_all = a.ctrl->grad_scale;
   const float abs_scale = fabsf(scale_all);
   const uint32_t sign = scale_all < 0.f ? 0x80008000u : 0u;
   const float log2_scale = __builtin_amdgcn_logf(abs_scale);  // -inf for a zero scale
 
-  u32x2_t gp[4][4][4];  // [ni][mi][q]: G of rows acc_row(mi, 4q .. 4q + 3), bf16 pairs
+  u32x2_t gp[kNI][4][4];  // [ni][mi][q]: G of rows acc_row(mi, 4q .. 4q + 3), bf16 pairs
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int64_t tok = n0 + wn * kWaveTile + ni * 32 + (lane & 31);
+  for (int ni = 0; ni < kNI; ++ni) {
+    const int64_t tok = n0 + wn * kWaveN + ni * 32 + (lane & 31);
     const bool tok_ok = tok < a.N;
     const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
     const bool valid = t != a.ignore_index;
@@ -260,7 +262,7 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
     // |scale| * exp(z - lse) = exp2(z log2e + c); an ignored token gets c = -inf
     const float c = valid ? log2_scale - lse2 : -INFINITY;
     const int64_t tl64 = (int64_t)t - (a.v_begin + vrow0);  // target row in this wave
-    const bool hit = valid && tl64 >= 0 && tl64 < kWaveTile;
+    const bool hit = valid && tl64 >= 0 && tl64 < kWaveM;
     const int tl = hit ? (int)tl64 : -1;
     const bool any_hit = __any(hit);
     float v[64];
@@ -302,10 +304,10 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
 #pragma unroll
   for (int pass = 0; pass < kTile / kPassTok; ++pass) {
     block_barrier();  // staging free: the previous pass (or tile) is done with it
-    if (wn == pass) {
+    if (wn * kWaveN / kPassTok == pass) {
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int row = ni * 32 + (lane & 31);  // token within the pass
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int row = wn * kWaveN - pass * kPassTok + ni * 32 + (lane & 31);  // token in the pass
         char* lrow = lds + row * kRowBytes + half * 8;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
@@ -376,14 +378,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs<T>& g, Acc& acc, in
       make_buffer(g.c + m0 * g.ldc + n0, (g.m - m0) * g.ldc * 4 - n0 * 4);
   const int run = tid & 63;                         // 16-byte run of a row (4 columns)
   const bool run_ok = n0 + 4 * run < g.n;
-  constexpr int kRowsPerThread = kEpiRows / 4;      // 4 waves, one row each at a time
+  constexpr int kRowsPerThread = kEpiRows / kWaves;  // every wave one row at a time
 
 #pragma unroll
   for (int pass = 0; pass < kTile / kEpiRows; ++pass) {
     const int row0 = pass * kEpiRows;
-    // rows of this thread: row0 + wave + 4 i; byte offsets from the tile's row 0
+    // rows of this thread: row0 + wave + kWaves i; byte offsets from the tile's row 0
     const uint32_t off0 = run_ok ? (uint32_t)(row0 + wave) * ldc4 + run * 16 : kOutOfRange;
-    const uint32_t step = run_ok ? 4 * ldc4 : 0u;
+    const uint32_t step = run_ok ? kWaves * ldc4 : 0u;
     constexpr int kEarly = kRowsPerThread / 2;  // C rows loaded before the staging writes
     u32x4_t old[kRowsPerThread];
     if constexpr (Accum) {
@@ -398,8 +400,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs<T>& g, Acc& acc, in
       for (int h = 0; h < 2; ++h) {
         const int mi = 2 * (pass % 2) + h;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int col = wn * kWaveTile + ni * 32 + (lane & 31);
+        for (int ni = 0; ni < kNI; ++ni) {
+          const int col = wn * kWaveN + ni * 32 + (lane & 31);
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int row = h * 32 + acc_row(0, e, lane);
@@ -413,7 +415,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs<T>& g, Acc& acc, in
     f32x4_t v[kRowsPerThread];
 #pragma unroll
     for (int i = 0; i < kRowsPerThread; ++i) {
-      const int row = wave + 4 * i;
+      const int row = wave + kWaves * i;
       v[i] = *reinterpret_cast<const f32x4_t*>(lds + epi_offset(row, run));
     }
     if constexpr (Accum) {

@@ -1,13 +1,17 @@
 // tile_engine.h - one 256x256 MFMA tile of C = A . B^T on gfx950 (CDNA4).
 //
-// A block of 256 threads (four wave64s in a 2x2 grid, each owning a 128x128
-// sub-tile of fp32 accumulators) walks K in stages of 64 bytes per row (32
-// bf16 or 16 f32 elements).  Stages are copied from global memory straight
-// into LDS with buffer_load ... lds (no register staging) into a ring of
-// kStages buffers, so a stage is copied kStages - 1 stages before it is read.
+// A block of 512 threads (eight wave64s in a 2x4 grid, two per SIMD, each
+// owning a 128x64 sub-tile of fp32 accumulators) walks K in stages of 64
+// bytes per row (32 bf16 or 16 f32 elements).  Two waves per SIMD let one
+// wave's MFMAs run while the other waits on an LDS read or on the texture
+// unit; LDS read bandwidth (about 240 B/clk per CU with eight waves, half
+// that with four) covers the 1.5x fragment reads this layout costs.  Stages
+// are copied from global memory straight into LDS with buffer_load ... lds
+// (no register staging) into a ring of kStages buffers, so a stage is copied
+// kStages - 1 stages before it is read.
 // The copies of a stage are spread over the MFMAs of the stage before: one
 // wave-wide copy after every fourth MFMA.  The texture unit takes many cycles
-// per 1 KiB copy and is shared by the CU's four waves, so copies issued in a
+// per 1 KiB copy and is shared by the CU's waves, so copies issued in a
 // burst stall every wave's MFMA issue at once; spread out, they hide behind
 // the MFMAs.  The lead given by the ring is what lets them be spread.
 // Fragments are read back from LDS as 16-byte K-runs that feed
@@ -43,8 +47,11 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 constexpr int kTile = 256;                 // block tile along M and along N
-constexpr int kWaveTile = 128;             // wave sub-tile along M and along N
-constexpr int kThreads = 256;              // four waves
+constexpr int kWaves = 8;                  // waves per block, 2 along M x kWaves / 2 along N
+constexpr int kWaveM = 128;                // wave sub-tile along M
+constexpr int kWaveN = kTile / (kWaves / 2);  // wave sub-tile along N
+constexpr int kNI = kWaveN / 32;           // 32-column MFMA tiles of a wave along N
+constexpr int kThreads = 64 * kWaves;
 constexpr int kStageRowBytes = 64;         // K bytes per row per stage
 constexpr int kSteps = kStageRowBytes / 32;   // k16 (bf16) / k8 (f32) steps per stage
 constexpr int kChunks = kStageRowBytes / 16;  // 16-byte chunks per row per stage
@@ -54,7 +61,7 @@ constexpr int kStages = 3;                 // ring of stages in LDS
 constexpr int kRingBytes = kStages * kStageBytes;
 constexpr int kStagingBytes = 64 * 1024;   // epilogue staging, after the ring
 constexpr int kLdsBytes = kRingBytes + kStagingBytes;
-constexpr int kCopiesPerWave = kOperandBytes / 1024 / 4;  // 1 KiB per wave-wide copy
+constexpr int kCopiesPerWave = kOperandBytes / 1024 / kWaves;  // 1 KiB per wave-wide copy
 constexpr int kRowsPerCopy = 1024 / kStageRowBytes;       // K-contiguous rows per copy
 static_assert(kStageRowBytes == 64 || kStageRowBytes == 128, "stage of 64 or 128 bytes per row");
 static_assert(kSteps % 2 == 0, "fragments alternate between two register sets");
@@ -153,7 +160,7 @@ struct Side<T, true> {
     rsrc = make_rsrc(op.base + mn0 * op.ld, (op.mn_ext - mn0) * op.ld * (int64_t)sizeof(T));
   }
   // Per-lane copy and fragment offsets (the same for every tile).
-  __device__ __forceinline__ void init_lanes(const Operand<T>& op, int wave, int lane, int wsub) {
+  __device__ __forceinline__ void init_lanes(const Operand<T>& op, int wave, int lane, int sub0) {
     const int64_t row_bytes = op.ld * (int64_t)sizeof(T);
     k_ext_bytes = op.k_ext * (int64_t)sizeof(T);
     const int rsub = lane / kChunks;  // row within a copy
@@ -167,7 +174,7 @@ struct Side<T, true> {
       const int row = kRowsPerCopy * (kCopiesPerWave * wave + i) + rsub;
       voff[i] = (uint32_t)(row * row_bytes) + kbyte[i & 1];
     }
-    const int frow = wsub * kWaveTile + (lane & 31);
+    const int frow = sub0 + (lane & 31);
 #pragma unroll
     for (int j = 0; j < kSteps; ++j) {
       const int ch = 2 * j + (lane >> 5);
@@ -175,8 +182,8 @@ struct Side<T, true> {
     }
   }
   __device__ __forceinline__ void init(const Operand<T>& op, int64_t mn0, int wave, int lane,
-                                       int wsub) {
-    init_lanes(op, wave, lane, wsub);
+                                       int sub0) {
+    init_lanes(op, wave, lane, sub0);
     retarget(op, mn0);
   }
   // Copy stage kt (K bytes [kt, kt + 1) * kStageRowBytes) to LDS address dst;
@@ -216,12 +223,12 @@ struct Side<__bf16, false> {
     mn0_bytes = mn0 * 2;
   }
   __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane,
-                                       int wsub) {
-    init_lanes(op, wave, lane, wsub);
+                                       int sub0) {
+    init_lanes(op, wave, lane, sub0);
     retarget(op, mn0);
   }
   __device__ __forceinline__ void init_lanes(const Operand<__bf16>& op, int wave, int lane,
-                                             int wsub) {
+                                             int sub0) {
     row_bytes = op.ld * 2;
     k_ext = op.k_ext;
 #pragma unroll
@@ -240,7 +247,7 @@ struct Side<__bf16, false> {
     const int kr = 8 * (g >> 1) + (jj >> 2);  // swz_mn depends on kr % 4 only
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      const int col = wsub * kWaveTile + mi * 32 + 16 * (g & 1) + 4 * (jj & 3);
+      const int col = sub0 + mi * 32 + 16 * (g & 1) + 4 * (jj & 3);
       const int c = (col >> 3) ^ swz_mn(kr);
       frag_off[mi] = (uint32_t)(kr * 512 + c * 16 + (col & 7) * 2);
     }
@@ -283,12 +290,12 @@ struct Side<float, false> {
     mn0_bytes = mn0 * 4;
   }
   __device__ __forceinline__ void init(const Operand<float>& op, int64_t mn0, int wave, int lane,
-                                       int wsub) {
-    init_lanes(op, wave, lane, wsub);
+                                       int sub0) {
+    init_lanes(op, wave, lane, sub0);
     retarget(op, mn0);
   }
   __device__ __forceinline__ void init_lanes(const Operand<float>& op, int wave, int lane,
-                                             int wsub) {
+                                             int sub0) {
     row_bytes = op.ld * 4;
     k_ext = op.k_ext;
 #pragma unroll
@@ -296,7 +303,7 @@ struct Side<float, false> {
       const int kr = kCopiesPerWave * wave + i;
       voff[i] = (uint32_t)(kr * row_bytes + lane * 16);
     }
-    frag_off = (uint32_t)((wsub * kWaveTile + (lane & 31)) * 4 + (lane >> 5) * 4 * 1024);
+    frag_off = (uint32_t)((sub0 + (lane & 31)) * 4 + (lane >> 5) * 4 * 1024);
   }
   __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
                                           int i) const {
@@ -350,11 +357,11 @@ struct Mfma<float> {
   }
 };
 
-// Accumulators of one wave: 4 x 4 MFMA tiles of 32 x 32.
+// Accumulators of one wave: 4 x kNI MFMA tiles of 32 x 32.
 // Element (mi, ni, e) of lane l sits at tile row
-//   wm*128 + mi*32 + (e/4)*8 + (l/32)*4 + e%4   and column  wn*128 + ni*32 + l%32.
+//   wm*kWaveM + mi*32 + (e/4)*8 + (l/32)*4 + e%4   and column  wn*kWaveN + ni*32 + l%32.
 struct Acc {
-  f32x16_t c[4][4];
+  f32x16_t c[4][kNI];
 };
 
 __device__ __forceinline__ int acc_row(int mi, int e, int lane) {
@@ -363,20 +370,21 @@ __device__ __forceinline__ int acc_row(int mi, int e, int lane) {
 
 template <typename T, bool AK, bool BK>
 struct Frags {
-  u32x4_t a[4], b[4];
+  static constexpr int kReads = 4 + kNI;
+  u32x4_t a[4], b[kNI];
   __device__ __forceinline__ void read(const Side<T, AK>& sa, const Side<T, BK>& sb,
                                        const char* stage, int j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = sa.frag(stage, i, j);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = sb.frag(stage + kOperandBytes, i, j);
+    for (int i = 0; i < kNI; ++i) b[i] = sb.frag(stage + kOperandBytes, i, j);
   }
-  // Read r of 8, in the order the MFMAs first use them: a0, b0..b3, a1..a3.
+  // Read r of kReads, in the order the MFMAs first use them: a0, all of b, a1..a3.
   __device__ __forceinline__ void read_one(const Side<T, AK>& sa, const Side<T, BK>& sb,
                                            const char* stage, int j, int r) {
     if (r == 0) a[0] = sa.frag(stage, 0, j);
-    else if (r <= 4) b[r - 1] = sb.frag(stage + kOperandBytes, r - 1, j);
-    else a[r - 4] = sa.frag(stage, r - 4, j);
+    else if (r <= kNI) b[r - 1] = sb.frag(stage + kOperandBytes, r - 1, j);
+    else a[r - kNI] = sa.frag(stage, r - kNI, j);
   }
 };
 
@@ -398,31 +406,6 @@ __device__ __forceinline__ int opaque(int x) {
 
 // Keeps the instruction scheduler from moving anything across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-
-// Half a stage: the 16 MFMAs of one k step (fragments `use`), with the 8
-// fragment reads of the next k step (into `fill`, step j of the stage at src)
-// after the first 8 MFMAs, and, with Copy, the 4 copies of one operand (side
-// cs, stage kc, to dst) after MFMAs 1, 5, 9 and 13.  Spreading the copies keeps
-// the MFMA pipe fed while the texture unit works through them; issued in a
-// burst, they would hold every wave of the CU at once.
-template <bool Reads, bool Copy, typename T, bool AK, bool BK, typename CS>
-__device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, BK>& sb,
-                                           const Frags<T, AK, BK>& use, Frags<T, AK, BK>& fill,
-                                           const char* src, int j, const CS& cs, uint32_t dst,
-                                           int64_t kc, int wave, bool live, Acc& acc) {
-  static_assert(kCopiesPerWave == 4, "one copy per four MFMAs");
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    acc.c[t / 4][t % 4] = Mfma<T>::run(use.a[t / 4], use.b[t % 4], acc.c[t / 4][t % 4]);
-    if constexpr (Reads) {
-      if (t < 8) fill.read_one(sa, sb, src, j, t);
-    }
-    if constexpr (Copy) {
-      if ((t & 3) == 1) cs.copy_one(dst, kc, wave, live, t >> 2);
-    }
-    sched_fence();
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Tile order and the persistent tile loop.
@@ -489,10 +472,10 @@ struct Cursor {
   }
 };
 
-// Half a stage: the 16 MFMAs of one k step (fragments `use`), with the 8
-// fragment reads of the next k step (into `fill`, step j of the stage at src)
-// after the first 8 MFMAs, and, with Copy, the 4 copies of one operand's
-// current stage after MFMAs 1, 5, 9 and 13.  Spreading the copies keeps the
+// Half a stage: the 4 kNI MFMAs of one k step (fragments `use`), with the
+// 4 + kNI fragment reads of the next k step (into `fill`, step j of the stage
+// at src) after the first MFMAs, and, with Copy, the kNI copies of one
+// operand's current stage after MFMAs 1, 5, 9, ... (one copy per four MFMAs).  Spreading the copies keeps the
 // MFMA pipe fed while the texture unit works through them; issued in a burst,
 // they would hold every wave of the CU at once.
 template <bool Reads, bool Copy, typename T, bool AK, bool BK, typename C>
@@ -500,12 +483,13 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
                                            const Frags<T, AK, BK>& use, Frags<T, AK, BK>& fill,
                                            const char* src, int j, const C& cur, uint32_t lds0,
                                            uint32_t off, int wave, int64_t tiles, Acc& acc) {
-  static_assert(kCopiesPerWave == 4, "one copy per four MFMAs");
+  static_assert(kCopiesPerWave == kNI, "one copy per four MFMAs");
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    acc.c[t / 4][t % 4] = Mfma<T>::run(use.a[t / 4], use.b[t % 4], acc.c[t / 4][t % 4]);
+  for (int t = 0; t < 4 * kNI; ++t) {
+    acc.c[t / kNI][t % kNI] =
+        Mfma<T>::run(use.a[t / kNI], use.b[t % kNI], acc.c[t / kNI][t % kNI]);
     if constexpr (Reads) {
-      if (t < 8) fill.read_one(sa, sb, src, j, t);
+      if (t < Frags<T, AK, BK>::kReads) fill.read_one(sa, sb, src, j, t);
     }
     if constexpr (Copy) {
       if ((t & 3) == 1) cur.copy_one(lds0, off, wave, tiles, t >> 2);
@@ -567,8 +551,8 @@ __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>&
 
   Cursor<T, AK> ca{{}, 0, 0, 0u};
   Cursor<T, BK> cb{{}, 0, 0, 0u};
-  ca.side.init(A, m0, wave, lane, wm);
-  cb.side.init(B, n0, wave, lane, wn);
+  ca.side.init(A, m0, wave, lane, wm * kWaveM);
+  cb.side.init(B, n0, wave, lane, wn * kWaveN);
   const Side<T, AK>& sa = ca.side;  // fragment offsets do not depend on the tile
   const Side<T, BK>& sb = cb.side;
 
@@ -592,13 +576,13 @@ __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>&
     {
       // per-lane offsets again, so that none of them is live across an epilogue
       const int l = opaque(lane);
-      ca.side.init_lanes(A, wave, l, wm);
-      cb.side.init_lanes(B, wave, l, wn);
+      ca.side.init_lanes(A, wave, l, wm * kWaveM);
+      cb.side.init_lanes(B, wave, l, wn * kWaveN);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc.c[r][c] = f32x16_t{};
+      for (int c = 0; c < kNI; ++c) acc.c[r][c] = f32x16_t{};
     f0.read(sa, sb, lds + buf * kStageBytes, 0);
     sched_fence();
     for (int64_t kt = 0; kt + 1 < nk; ++kt) {
