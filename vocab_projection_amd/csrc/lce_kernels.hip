@@ -137,10 +137,10 @@ template <> struct GPack<float> {
   }
 };
 
-// The gradient strip leaves through LDS in passes of kGradTok tokens: the
-// waves holding those tokens write their G values as token rows, then every
-// thread stores whole 16-byte runs of a row, so a wave writes 512 (bf16) or
-// 1024 (f32) contiguous bytes of G per instruction.
+// f32 gradient strips leave through LDS in passes of kTok tokens: the waves
+// holding those tokens write their G values as token rows, then every thread
+// stores whole 16-byte runs of a row, so a wave writes 1024 contiguous bytes
+// of G per instruction.  (bf16 strips use the packed path below.)
 template <typename T> struct GradStage {
   static constexpr int kTok = sizeof(T) == 2 ? 64 : 32;       // tokens per pass
   static constexpr int kRowBytes = kTile * (int)sizeof(T);      // 256 vocabulary columns
@@ -348,10 +348,10 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
 //
 // The epilogue goes through the LDS staging area in four passes of 64 rows
 // (1 KiB each, unpadded: the 16-byte chunk index is XOR-swizzled by the row,
-// so the two rows of an MFMA-layout write never share banks): the two waves
-// that hold those rows write them, then all 256 threads move whole 16-byte
-// runs of each row, so that every wave reads and writes 1 KiB of one row of
-// C per instruction.  With Accum a pass issues half of its loads of C before
+// so the two rows of an MFMA-layout write never share banks): the waves that
+// hold those rows write them, then all threads move whole 16-byte runs of
+// each row, so that every wave reads and writes 1 KiB of one row of C per
+// instruction.  With Accum a pass issues half of its loads of C before
 // the staging writes, so that their latency hides behind them.
 // ---------------------------------------------------------------------------
 constexpr int kEpiRows = 64;                        // rows of C per pass

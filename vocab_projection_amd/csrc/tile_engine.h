@@ -63,20 +63,15 @@ constexpr int kStagingBytes = 64 * 1024;   // epilogue staging, after the ring
 constexpr int kLdsBytes = kRingBytes + kStagingBytes;
 constexpr int kCopiesPerWave = kOperandBytes / 1024 / kWaves;  // 1 KiB per wave-wide copy
 constexpr int kRowsPerCopy = 1024 / kStageRowBytes;       // K-contiguous rows per copy
-static_assert(kStageRowBytes == 64 || kStageRowBytes == 128, "stage of 64 or 128 bytes per row");
-static_assert(kSteps % 2 == 0, "fragments alternate between two register sets");
+static_assert(kStageRowBytes == 64 && kSteps == 2, "stages of two 16-deep k steps");
 static_assert(kStages >= 3 && kLdsBytes <= 160 * 1024, "ring and staging fit in LDS");
 constexpr uint32_t kOutOfRange = 0x80000000u;           // voffset that reads zeros
 constexpr int kRsrcWord3 = 0x00020000;                  // raw buffer, gfx9 family
 
 // Swizzle of a K-contiguous stage: physical chunk = logical chunk ^ swz_k(row)
-// (a function of row bits 0..3 only).
+// (a function of row bits 1..3 only).
 __device__ __forceinline__ int swz_k(int r) {
-  if constexpr (kChunks == 8) {
-    return ((r ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1) | (((r >> 1) & 1) << 2);
-  } else {
-    return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
-  }
+  return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
 }
 // Swizzle of an MN-contiguous bf16 stage: physical chunk = chunk ^ swz_mn(k-row).
 __device__ __forceinline__ int swz_mn(int k) {
@@ -151,7 +146,7 @@ template <typename T>
 struct Side<T, true> {
   u32x4_t rsrc;
   uint32_t voff[kCopiesPerWave];
-  uint32_t kbyte[2];     // byte column of this lane's logical chunk (even / odd copies)
+  uint32_t kbyte;        // byte column of this lane's logical chunk
   int64_t k_ext_bytes;
   uint32_t frag_off[kSteps];  // per k step: byte offset of this lane's fragment (mi = 0)
 
@@ -164,15 +159,13 @@ struct Side<T, true> {
     const int64_t row_bytes = op.ld * (int64_t)sizeof(T);
     k_ext_bytes = op.k_ext * (int64_t)sizeof(T);
     const int rsub = lane / kChunks;  // row within a copy
-    // swz_k depends on row bits 0..3; with 8 rows per copy bit 3 is the parity
-    // of the copy index, with 16 it is fixed by the lane
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      kbyte[p] = (uint32_t)(((lane % kChunks) ^ swz_k(rsub + kRowsPerCopy * p)) * 16);
+    // swz_k depends on row bits 1..3, which the lane fixes (16 rows per copy)
+    static_assert(kRowsPerCopy == 16, "one swizzle per lane");
+    kbyte = (uint32_t)(((lane % kChunks) ^ swz_k(rsub)) * 16);
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) {
       const int row = kRowsPerCopy * (kCopiesPerWave * wave + i) + rsub;
-      voff[i] = (uint32_t)(row * row_bytes) + kbyte[i & 1];
+      voff[i] = (uint32_t)(row * row_bytes) + kbyte;
     }
     const int frow = sub0 + (lane & 31);
 #pragma unroll
@@ -193,7 +186,7 @@ struct Side<T, true> {
                                           int i) const {
     const int64_t k0 = kt * kStageRowBytes;
     const uint32_t soff = live ? (uint32_t)k0 : 0u;
-    const bool ok = live && k0 + kbyte[i & 1] < k_ext_bytes;
+    const bool ok = live && k0 + kbyte < k_ext_bytes;
     dma16(rsrc, dst + (kCopiesPerWave * wave + i) * 1024, ok ? voff[i] : kOutOfRange, soff);
   }
   __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
