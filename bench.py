@@ -64,7 +64,7 @@ def ensure_built():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
 
