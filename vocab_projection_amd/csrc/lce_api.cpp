@@ -185,6 +185,10 @@ lce_status_t fold_bwd(const Plan& pl, const void* hidden, const void* weight_str
   if (steps & LCE_STEP_GRAD) {
     if ((s = launched(lce::launch_strip_grad<T>(a, st))) != LCE_OK) return s;
   }
+  if ((steps & LCE_STEP_DHIDDEN) && (steps & LCE_STEP_DWEIGHT)) {
+    return launched(lce::launch_dh_dw<T>(a.g_strip, pl.ldg, a.weight_strip, a.hidden, v_len, pl.N,
+                                         pl.H, d_hidden, accumulate, d_weight_strip, st));
+  }
   if (steps & LCE_STEP_DHIDDEN) {
     s = launched(lce::launch_dh<T>(a.g_strip, pl.ldg, a.weight_strip, v_len, pl.N, pl.H, d_hidden,
                                    accumulate, st));

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) 
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<T> B{a.hidden, a.H, a.N, a.H};
-  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m};
+  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x};
   run_tiles<T, true, true>(A, B, a.H, grid, lds,
                            [&](Acc& acc, int64_t m0, int64_t n0, char*) {
                              lse_epilogue(a, acc, m0, n0);
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<T> B{a.hidden, a.H, a.N, a.H};
-  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m};
+  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x};
   run_tiles<T, true, true>(A, B, a.H, grid, lds,
                            [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
                              grad_epilogue(a, acc, m0, n0, staging);
@@ -438,11 +438,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g)
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const Operand<T> A{g.a, g.lda, g.a_mn_ext, g.a_k_ext};
   const Operand<T> B{g.b, g.ldb, g.b_mn_ext, g.b_k_ext};
-  const TileGrid grid{g.m_tiles, g.n_tiles, g.group_m};
+  const TileGrid grid{g.m_tiles, g.n_tiles, g.group_m, blockIdx.x, gridDim.x};
   run_tiles<T, AK, BK>(A, B, g.k_len, grid, lds,
                        [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
                          gemm_epilogue<T, Accum>(g, acc, m0, n0, staging);
                        });
+}
+
+// dH and dW of one strip in one launch: blocks [0, split) form dH
+// (K-contiguous G, MN-contiguous W_s), the rest dW (MN-contiguous G and h).
+// Both read G and write disjoint outputs, so the compute units can be shared
+// out by work when one of them alone has too few tiles to fill them.
+template <typename T, bool AccumDh>
+__global__ __launch_bounds__(kThreads, 1) void gemm_dh_dw_kernel(GemmArgs<T> dh, GemmArgs<T> dw,
+                                                                 int64_t split) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int64_t b = blockIdx.x;
+  if (b < split) {
+    const Operand<T> A{dh.a, dh.lda, dh.a_mn_ext, dh.a_k_ext};
+    const Operand<T> B{dh.b, dh.ldb, dh.b_mn_ext, dh.b_k_ext};
+    const TileGrid grid{dh.m_tiles, dh.n_tiles, dh.group_m, b, split};
+    run_tiles<T, true, false>(A, B, dh.k_len, grid, lds,
+                              [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
+                                gemm_epilogue<T, AccumDh>(dh, acc, m0, n0, staging);
+                              });
+  } else {
+    const Operand<T> A{dw.a, dw.lda, dw.a_mn_ext, dw.a_k_ext};
+    const Operand<T> B{dw.b, dw.ldb, dw.b_mn_ext, dw.b_k_ext};
+    const TileGrid grid{dw.m_tiles, dw.n_tiles, dw.group_m, b - split, gridDim.x - split};
+    run_tiles<T, false, false>(A, B, dw.k_len, grid, lds,
+                               [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
+                                 gemm_epilogue<T, false>(dw, acc, m0, n0, staging);
+                               });
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -626,28 +654,91 @@ static hipError_t launch_gemm(GemmArgs<T> g, hipStream_t st) {
 
 // dH[N, H] (+)= G[N, :v_len] . W_s[v_len, H]: M = tokens, N = H, K = strip rows.
 template <typename T>
-hipError_t launch_dh(const T* g_strip, int64_t ldg, const T* w_strip, int64_t v_len, int64_t n_tok,
-                     int64_t h, float* d_hidden, int accumulate, hipStream_t st) {
+static GemmArgs<T> dh_args(const T* g_strip, int64_t ldg, const T* w_strip, int64_t v_len,
+                           int64_t n_tok, int64_t h, float* d_hidden) {
   GemmArgs<T> g{};
   g.a = g_strip; g.lda = ldg; g.a_mn_ext = n_tok; g.a_k_ext = v_len;   // K-contiguous
   g.b = w_strip; g.ldb = h;   g.b_mn_ext = h;     g.b_k_ext = v_len;   // MN-contiguous
   g.k_len = v_len;
   g.c = d_hidden; g.ldc = h; g.m = n_tok; g.n = h;
-  return accumulate ? launch_gemm<T, true, false, true>(g, st)
-                    : launch_gemm<T, true, false, false>(g, st);
+  g.m_tiles = cdiv(g.m, kTile);
+  g.n_tiles = cdiv(g.n, kTile);
+  g.group_m = kGemmGroupM;
+  return g;
 }
 
 // dW_s[v_len, H] = G[:, :v_len]^T . h: M = strip rows, N = H, K = tokens.
 template <typename T>
-hipError_t launch_dw(const T* g_strip, int64_t ldg, const T* hidden, int64_t v_len, int64_t n_tok,
-                     int64_t h, float* d_weight_strip, hipStream_t st) {
+static GemmArgs<T> dw_args(const T* g_strip, int64_t ldg, const T* hidden, int64_t v_len,
+                           int64_t n_tok, int64_t h, float* d_weight_strip) {
   GemmArgs<T> g{};
   const int64_t cols = cdiv(v_len, 8) * 8;  // chunk-aligned; the pad columns of G are zero
   g.a = g_strip; g.lda = ldg; g.a_mn_ext = cols; g.a_k_ext = n_tok;    // MN-contiguous
   g.b = hidden;  g.ldb = h;   g.b_mn_ext = h;    g.b_k_ext = n_tok;    // MN-contiguous
   g.k_len = n_tok;
   g.c = d_weight_strip; g.ldc = h; g.m = v_len; g.n = h;
-  return launch_gemm<T, false, false, false>(g, st);
+  g.m_tiles = cdiv(g.m, kTile);
+  g.n_tiles = cdiv(g.n, kTile);
+  g.group_m = kGemmGroupM;
+  return g;
+}
+
+template <typename T>
+hipError_t launch_dh(const T* g_strip, int64_t ldg, const T* w_strip, int64_t v_len, int64_t n_tok,
+                     int64_t h, float* d_hidden, int accumulate, hipStream_t st) {
+  const GemmArgs<T> g = dh_args(g_strip, ldg, w_strip, v_len, n_tok, h, d_hidden);
+  return accumulate ? launch_gemm<T, true, false, true>(g, st)
+                    : launch_gemm<T, true, false, false>(g, st);
+}
+
+template <typename T>
+hipError_t launch_dw(const T* g_strip, int64_t ldg, const T* hidden, int64_t v_len, int64_t n_tok,
+                     int64_t h, float* d_weight_strip, hipStream_t st) {
+  return launch_gemm<T, false, false, false>(
+      dw_args(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip), st);
+}
+
+// Stages each compute unit runs (the longest block) when `blocks` blocks share
+// `tiles` tiles of `nk` stages.
+static int64_t stage_load(int64_t tiles, int64_t nk, int64_t blocks) {
+  return cdiv(tiles, blocks) * nk;
+}
+
+template <typename T>
+hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T* hidden,
+                        int64_t v_len, int64_t n_tok, int64_t h, float* d_hidden, int accumulate,
+                        float* d_weight_strip, hipStream_t st) {
+  const GemmArgs<T> dh = dh_args(g_strip, ldg, w_strip, v_len, n_tok, h, d_hidden);
+  const GemmArgs<T> dw = dw_args(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip);
+  const int64_t t_dh = dh.m_tiles * dh.n_tiles, nk_dh = stages_of<T>(dh.k_len);
+  const int64_t t_dw = dw.m_tiles * dw.n_tiles, nk_dw = stages_of<T>(dw.k_len);
+  const int64_t p = persistent_blocks();
+  // Both persistent (more stages per tile than the ring holds) and the shared
+  // launch strictly shorter than two launches: share; else two launches.
+  int64_t best_split = 0, best = stage_load(t_dh, nk_dh, p) + stage_load(t_dw, nk_dw, p);
+  if (nk_dh > kStages && nk_dw > kStages) {
+    for (int64_t split = kXcds; split < p; split += kXcds) {
+      const int64_t a = stage_load(t_dh, nk_dh, split), b = stage_load(t_dw, nk_dw, p - split);
+      const int64_t c = a > b ? a : b;
+      if (c < best) { best = c; best_split = split; }
+    }
+  }
+  if (best_split == 0) {
+    hipError_t e = launch_dh(g_strip, ldg, w_strip, v_len, n_tok, h, d_hidden, accumulate, st);
+    if (e != hipSuccess) return e;
+    return launch_dw(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip, st);
+  }
+  const void* fn = accumulate ? reinterpret_cast<const void*>(&gemm_dh_dw_kernel<T, true>)
+                              : reinterpret_cast<const void*>(&gemm_dh_dw_kernel<T, false>);
+  hipError_t e = set_lds<T>(fn);
+  if (e != hipSuccess) return e;
+  if (accumulate)
+    hipLaunchKernelGGL((gemm_dh_dw_kernel<T, true>), dim3((unsigned)p), dim3(kThreads), kLdsBytes,
+                       st, dh, dw, best_split);
+  else
+    hipLaunchKernelGGL((gemm_dh_dw_kernel<T, false>), dim3((unsigned)p), dim3(kThreads),
+                       kLdsBytes, st, dh, dw, best_split);
+  return hipGetLastError();
 }
 
 hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st) {
@@ -687,6 +778,11 @@ template hipError_t launch_dh<float>(const float*, int64_t, const float*, int64_
                                      int64_t, float*, int, hipStream_t);
 template hipError_t launch_dw<__bf16>(const __bf16*, int64_t, const __bf16*, int64_t, int64_t,
                                       int64_t, float*, hipStream_t);
+template hipError_t launch_dh_dw<__bf16>(const __bf16*, int64_t, const __bf16*, const __bf16*,
+                                         int64_t, int64_t, int64_t, float*, int, float*,
+                                         hipStream_t);
+template hipError_t launch_dh_dw<float>(const float*, int64_t, const float*, const float*, int64_t,
+                                        int64_t, int64_t, float*, int, float*, hipStream_t);
 template hipError_t launch_dw<float>(const float*, int64_t, const float*, int64_t, int64_t,
                                      int64_t, float*, hipStream_t);
 

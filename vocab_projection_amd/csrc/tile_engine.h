@@ -409,21 +409,23 @@ constexpr int kXcds = 8;  // blocks are dispatched to the 8 XCDs round-robin
 // group N advances after every group_m tiles, so that consecutive tiles share
 // operand rows.  Each XCD (block b runs on XCD b % 8) is given one contiguous
 // range of that order, so the tiles resident on one XCD at the same time are
-// neighbours and share its L2.  Block b takes the tiles of virtual blocks
-// b, b + G, b + 2G, ... (G blocks; G is the tile count or a multiple of 8, so
-// that every virtual block of b maps to b's XCD).
+// neighbours and share its L2.  Block `block` of the `blocks` that work on
+// this output takes the tiles of virtual blocks block, block + G, block + 2G,
+// ... (G = blocks; G is the tile count or a multiple of 8, and the first block
+// of the output sits at a multiple of 8 in the grid, so that every virtual
+// block maps to the XCD of its block).
 struct TileGrid {
   int64_t m_tiles, n_tiles, group_m;
+  int64_t block, blocks;
 
   __device__ __forceinline__ int64_t total() const { return m_tiles * n_tiles; }
-  // Tiles taken by this block.
+  // Tiles taken by this block (zero if it is past the last tile).
   __device__ __forceinline__ int64_t count() const {
-    const int64_t g = gridDim.x;
-    return (total() - blockIdx.x + g - 1) / g;
+    return (total() - block + blocks - 1) / blocks;
   }
   // First row and column of this block's i-th tile.
   __device__ __forceinline__ void coords(int64_t i, int64_t* m0, int64_t* n0) const {
-    const int64_t b = blockIdx.x + i * (int64_t)gridDim.x;
+    const int64_t b = block + i * blocks;
     const int64_t x = b % kXcds, j = b / kXcds;
     const int64_t q = total() / kXcds, r = total() % kXcds;
     const int64_t t = x * q + (x < r ? x : r) + j;  // a bijection of [0, total)
@@ -538,6 +540,7 @@ __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>&
   char* const staging = lds + kRingBytes;
   const int64_t nk = (k_len + kStageK - 1) / kStageK;
   const int64_t tiles = grid.count();
+  if (tiles == 0) return;  // more blocks than tiles for this output
 
   int64_t m0, n0, next_m0, next_n0;  // this tile, and the next one
   grid.coords(0, &m0, &n0);
