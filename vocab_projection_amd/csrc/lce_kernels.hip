@@ -227,17 +227,22 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
   }
 }
 
-// bf16 strips: G for the whole tile is packed into VGPRs by all waves at
-// once (per element one FMA, one exp2 and half a pack: the token's |scale| is
-// folded into the exponent, its sign applied to the packed bits), then leaves
-// in two passes of 128 tokens through the 64 KiB staging area: 128 rows of
-// 512 bytes whose 16-byte chunks are XOR-swizzled by the row, so that neither
-// the MFMA-layout writes nor the row reads pile onto a few banks.
+// bf16 strips: G leaves in kNI passes through the 64 KiB staging area, pass
+// p holding the MFMA column block ni = p of every wave: 32 tokens per wave
+// column, (kWaves / 2) x 32 = 128 tokens, as 128 rows of 512 bytes whose
+// 16-byte chunks are XOR-swizzled by the row, so that neither the
+// MFMA-layout writes nor the row reads pile onto a few banks.  Every wave
+// computes its part of a pass straight into staging (per element one FMA,
+// one exp2 and half a pack: the token's |scale| is folded into the exponent,
+// its sign applied to the packed bits), so the accumulators of a column block
+// die in its pass and no packed copy of G is held: the kernel stays within
+// its registers.  (A spill would bring scratch loads, and their waits drain
+// every copy and store in flight.)  Targets and lse are loaded before any
+// store, so waiting for them never waits for this tile's stores.
 __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& acc, int64_t m0,
                                               int64_t n0, char* lds) {
   constexpr int kRowBytes = kTile * 2;        // 256 bf16 vocabulary columns
-  constexpr int kPassTok = 128;               // tokens per pass
-  static_assert(kPassTok % kWaveN == 0, "a pass holds whole wave columns");
+  constexpr int kPassTok = kWaves / 2 * 32;   // tokens per pass: one 32-column block per wave column
   static_assert(kPassTok * kRowBytes <= kStagingBytes, "staging fits in LDS");
   const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
   const int lane = tid & 63;
@@ -246,12 +251,17 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
   const int half = lane >> 5;
   const int64_t vrow0 = m0 + wm * kWaveM;
   const bool full = vrow0 + kWaveM <= a.v_len;  // no strip rows past v_len in this wave
+  // strip rows of this wave below v_len (only used when !full, then < kWaveM)
+  const int rows_left = full ? kWaveM : (int)max<int64_t>(a.v_len - vrow0, 0);
+  const int r_lane = (lane >> 5) * 4;  // acc_row(mi, e, lane) - acc_row(mi, e, 0)
   const float scale_all = a.ctrl->grad_scale;
   const float abs_scale = fabsf(scale_all);
   const uint32_t sign = scale_all < 0.f ? 0x80008000u : 0u;
   const float log2_scale = __builtin_amdgcn_logf(abs_scale);  // -inf for a zero scale
 
-  u32x2_t gp[kNI][4][4];  // [ni][mi][q]: G of rows acc_row(mi, 4q .. 4q + 3), bf16 pairs
+  float c[kNI];   // |scale| * exp(z - lse) = exp2(z log2e + c); an ignored token gets c = -inf
+  int tl[kNI];    // target row in this wave, or -1
+  bool any_hit[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
     const int64_t tok = n0 + wn * kWaveN + ni * 32 + (lane & 31);
@@ -259,41 +269,11 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
     const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
     const bool valid = t != a.ignore_index;
     const float lse2 = (tok_ok ? a.lse[tok] : 0.f) * kLog2e;
-    // |scale| * exp(z - lse) = exp2(z log2e + c); an ignored token gets c = -inf
-    const float c = valid ? log2_scale - lse2 : -INFINITY;
-    const int64_t tl64 = (int64_t)t - (a.v_begin + vrow0);  // target row in this wave
+    c[ni] = valid ? log2_scale - lse2 : -INFINITY;
+    const int64_t tl64 = (int64_t)t - (a.v_begin + vrow0);
     const bool hit = valid && tl64 >= 0 && tl64 < kWaveM;
-    const int tl = hit ? (int)tl64 : -1;
-    const bool any_hit = __any(hit);
-    float v[64];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        v[mi * 16 + e] = fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, c));
-    if (!full) {
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          v[mi * 16 + e] = vrow0 + acc_row(mi, e, lane) < a.v_len ? v[mi * 16 + e] : 0.f;
-    }
-    if (any_hit) {
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          v[mi * 16 + e] = acc_row(mi, e, lane) == tl ? v[mi * 16 + e] - abs_scale : v[mi * 16 + e];
-    }
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float* w = &v[mi * 16 + 4 * q];
-        const u32x2_t p = GPack<__bf16>::pack(w[0], w[1], w[2], w[3]);
-        gp[ni][mi][q] = u32x2_t{p[0] ^ sign, p[1] ^ sign};
-      }
-    sched_fence();
+    tl[ni] = hit ? (int)tl64 : -1;
+    any_hit[ni] = __any(hit);
   }
 
   // G rows n0.. of the strip buffer from column m0: byte offset
@@ -302,21 +282,44 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
   const __amdgpu_buffer_rsrc_t gbuf =
       make_buffer(a.g_strip + n0 * a.ldg + m0, (a.N - n0) * row_bytes - m0 * 2);
 #pragma unroll
-  for (int pass = 0; pass < kTile / kPassTok; ++pass) {
+  for (int ni = 0; ni < kNI; ++ni) {
     block_barrier();  // staging free: the previous pass (or tile) is done with it
-    if (wn * kWaveN / kPassTok == pass) {
+    {
+      float v[64];
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) {
-        const int row = wn * kWaveN - pass * kPassTok + ni * 32 + (lane & 31);  // token in the pass
-        char* lrow = lds + row * kRowBytes + half * 8;
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          v[mi * 16 + e] = fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, c[ni]));
+      // Row tests against the lane's row offset: acc_row(mi, e, lane) =
+      // acc_row(mi, e, 0) + r_lane, so each compares one VGPR with a constant.
+      if (!full) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int chunk = wm * 16 + mi * 4 + q;  // 16-byte chunk of columns
-            *reinterpret_cast<u32x2_t*>(lrow + ((chunk ^ (row & 31)) * 16)) = gp[ni][mi][q];
-          }
+          for (int e = 0; e < 16; ++e)
+            v[mi * 16 + e] = r_lane < rows_left - acc_row(mi, e, 0) ? v[mi * 16 + e] : 0.f;
       }
+      if (any_hit[ni]) {
+        const int d = tl[ni] - r_lane;  // the target's row minus the lane's offset
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            v[mi * 16 + e] = d == acc_row(mi, e, 0) ? v[mi * 16 + e] - abs_scale : v[mi * 16 + e];
+      }
+      const int row = wn * 32 + (lane & 31);  // staging row of this lane's token
+      char* lrow = lds + row * kRowBytes + half * 8;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float* w = &v[mi * 16 + 4 * q];
+          const u32x2_t pk = GPack<__bf16>::pack(w[0], w[1], w[2], w[3]);
+          const int chunk = wm * 16 + mi * 4 + q;  // 16-byte chunk of columns
+          *reinterpret_cast<u32x2_t*>(lrow + ((chunk ^ (row & 31)) * 16)) =
+              u32x2_t{pk[0] ^ sign, pk[1] ^ sign};
+        }
     }
     block_barrier();
     const int run = tid & 31;  // 16-byte run of a row
@@ -325,9 +328,12 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
       const int row = (tid >> 5) + (kThreads / 32) * i;
       const u32x4_t val =
           *reinterpret_cast<const u32x4_t*>(lds + row * kRowBytes + ((run ^ (row & 31)) * 16));
-      const uint32_t off = (uint32_t)((pass * kPassTok + row) * row_bytes) + run * 16;
+      // staging row -> token: wave column row / 32, column block ni, lane row % 32
+      const int tok = (row >> 5) * kWaveN + ni * 32 + (row & 31);
+      const uint32_t off = (uint32_t)(tok * row_bytes) + run * 16;
       __builtin_amdgcn_raw_buffer_store_b128(val, gbuf, off, 0, 0);
     }
+    sched_fence();
   }
 }
 
