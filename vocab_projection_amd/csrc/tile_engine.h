@@ -519,12 +519,14 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
 // tile per block (the copies past it are dead).
 //
 // The epilogue's stores (and loads) share vmcnt with the copies.  A counted
-// wait vmcnt(n), n = copies issued after the awaited ones, stays exact: loads
+// wait vmcnt(n), n = copies issued after the awaited ones, is safe: loads
 // complete in issue order among themselves, so while an awaited copy is
-// outstanding so is every later copy, and the count cannot drop to n;
-// uncounted later loads only make the wait stricter, and stores, which may
-// complete in any order relative to loads, are not counted at all.  So the
-// epilogue's stores drain behind the next tile's MFMAs.
+// outstanding so is every later copy, and the count cannot drop to n.  Any
+// other operation in flight (a store, an uncounted load) only makes the wait
+// stricter: stores may complete out of order with respect to loads, so they
+// cannot be counted in n.  The first wait after an epilogue (half a stage
+// into the next tile) therefore also waits for the epilogue's stores to be
+// acknowledged.
 template <typename T, bool AK, bool BK, typename Epi>
 __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int64_t k_len,
                                           const TileGrid& grid, char* lds, Epi&& epi) {
