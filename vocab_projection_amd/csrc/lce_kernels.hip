@@ -33,7 +33,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Forward strip: MFMA M = vocabulary rows of the strip, N = tokens, K = H.
 // ---------------------------------------------------------------------------
 // Per token of the tile and per 128 strip rows of a wave: (max, sum of
-// exp(z - max)) to partials, and the target logit to z_target.
+// exp(z - max)) to partials, and the target logit to z_target.  A token's
+// 128 rows of a wave sit in the four lanes l % 16 + 16 h (h = 0..3), 32
+// values each.
 template <typename T>
 __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, Acc& acc, int64_t m0,
                                              int64_t n0) {
@@ -48,52 +50,54 @@ __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, Acc& acc, in
   const int nrows = rows_left < kWaveM ? (int)rows_left : kWaveM;
   const bool full = nrows == kWaveM;
   const int64_t blk = vrow0 / kWaveM;
-  const int half = lane >> 5;
+  const int r_lane = (lane >> 4) * 4;  // acc_row(mi, e, lane) - acc_row(mi, e, 0)
 
-  // One 32-token column block (ni) at a time, so that only its 64 values per
+  // One 16-token column block (ni) at a time, so that only its 32 values per
   // lane are held in VGPRs.
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
-    const int64_t tok = n0 + wn * kWaveN + ni * 32 + (lane & 31);
+    const int64_t tok = n0 + wn * kWaveN + ni * kMfma + (lane & 15);
     const bool tok_ok = tok < a.N;
-    float v[64];
+    float v[4 * kMI];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[mi * 16 + e] = acc.c[mi][ni][e];
+      for (int e = 0; e < 4; ++e) v[mi * 4 + e] = acc.c[mi][ni][e];
     if (!full) {
       // rows past the strip's end: -inf adds nothing to the max or the sum
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          v[mi * 16 + e] = acc_row(mi, e, lane) >= nrows ? -INFINITY : v[mi * 16 + e];
+        for (int e = 0; e < 4; ++e)
+          v[mi * 4 + e] = r_lane >= nrows - acc_row(mi, e, 0) ? -INFINITY : v[mi * 4 + e];
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < 64; ++q) mx = fmaxf(mx, v[q]);
+    for (int q = 0; q < 4 * kMI; ++q) mx = fmaxf(mx, v[q]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mscaled = mx * kLog2e;
     float sum = 0.f;
 #pragma unroll
-    for (int q = 0; q < 64; ++q) sum += fast_exp2(__builtin_fmaf(v[q], kLog2e, -mscaled));
+    for (int q = 0; q < 4 * kMI; ++q) sum += fast_exp2(__builtin_fmaf(v[q], kLog2e, -mscaled));
+    sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
-    if (half == 0 && tok_ok) a.partials[blk * a.N + tok] = float2{mx, sum};
+    if (lane < 16 && tok_ok) a.partials[blk * a.N + tok] = float2{mx, sum};
 
     // Target logit: at most one (row, token) pair of the whole strip matches.
     const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
     const int64_t local = (int64_t)t - (a.v_begin + vrow0);
     const bool hit = t != a.ignore_index && local >= 0 && local < nrows;
     if (__any(hit)) {
-      const int lr = (int)local;
+      const int d = hit ? (int)local - r_lane : -1;  // acc_row(mi, e, 0) of the target, if here
       float zt = 0.f;
       bool mine = false;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const bool eq = hit && acc_row(mi, e, lane) == lr;
-          zt = eq ? v[mi * 16 + e] : zt;
+        for (int e = 0; e < 4; ++e) {
+          const bool eq = d == acc_row(mi, e, 0);
+          zt = eq ? v[mi * 4 + e] : zt;
           mine = mine || eq;
         }
       if (mine) a.z_target[tok] = zt;
@@ -142,7 +146,7 @@ template <> struct GPack<float> {
 // stores whole 16-byte runs of a row, so a wave writes 1024 contiguous bytes
 // of G per instruction.  (bf16 strips use the packed path below.)
 template <typename T> struct GradStage {
-  static constexpr int kTok = sizeof(T) == 2 ? 64 : 32;       // tokens per pass
+  static constexpr int kTok = 32;                               // tokens per pass
   static constexpr int kRowBytes = kTile * (int)sizeof(T);      // 256 vocabulary columns
   static constexpr int kStride = kRowBytes + 16;                // padded LDS row
   static constexpr int kRunsPerRow = kRowBytes / 16;
@@ -168,12 +172,12 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
   const __amdgpu_buffer_rsrc_t gbuf = make_buffer(
       a.g_strip + n0 * a.ldg + m0, (a.N - n0) * row_bytes - m0 * (int64_t)sizeof(T));
   static_assert(S::kTok <= kWaveN && kWaveN % S::kTok == 0, "a pass lies in one wave column");
-  constexpr int kNiPerPass = S::kTok / 32;
+  constexpr int kNiPerPass = S::kTok / kMfma;
 
   // G for every element, in place (all waves at once).
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
-    const int64_t tok = n0 + wn * kWaveN + ni * 32 + (lane & 31);
+    const int64_t tok = n0 + wn * kWaveN + ni * kMfma + (lane & 15);
     const bool tok_ok = tok < a.N;
     const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
     const float sc = t != a.ignore_index ? scale_all : 0.f;
@@ -183,9 +187,9 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
     const int tl = hit ? (int)tl64 : -1;
     const bool any_hit = __any(hit);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < 4; ++e) {
         const int r = acc_row(mi, e, lane);
         float g = sc * fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, -lse2));
         if (!full) g = (vrow0 + r < a.v_len) ? g : 0.f;
@@ -201,18 +205,16 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
     if (wn == tok_base / kWaveN) {
 #pragma unroll
       for (int nj = 0; nj < kNiPerPass; ++nj) {
-        const int ni = (tok_base % kWaveN) / 32 + nj;
-        const int tok_local = wn * kWaveN + ni * 32 + (lane & 31);
+        const int ni = (tok_base % kWaveN) / kMfma + nj;
+        const int tok_local = wn * kWaveN + ni * kMfma + (lane & 15);
         char* lrow = lds + (tok_local - tok_base) * S::kStride +
-                     (wm * kWaveM + (lane >> 5) * 4) * (int)sizeof(T);
+                     (wm * kWaveM + (lane >> 4) * 4) * (int)sizeof(T);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x16_t& c = acc.c[mi][ni];
-            *reinterpret_cast<typename GPack<T>::type*>(lrow + (mi * 32 + q * 8) * (int)sizeof(T)) =
-                GPack<T>::pack(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
-          }
+        for (int mi = 0; mi < kMI; ++mi) {
+          const f32x4_t& c = acc.c[mi][ni];
+          *reinterpret_cast<typename GPack<T>::type*>(lrow + mi * kMfma * (int)sizeof(T)) =
+              GPack<T>::pack(c[0], c[1], c[2], c[3]);
+        }
       }
     }
     block_barrier();
@@ -227,10 +229,10 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
   }
 }
 
-// bf16 strips: G leaves in kNI passes through the 64 KiB staging area, pass
-// p holding the MFMA column block ni = p of every wave: 32 tokens per wave
-// column, (kWaves / 2) x 32 = 128 tokens, as 128 rows of 512 bytes whose
-// 16-byte chunks are XOR-swizzled by the row, so that neither the
+// bf16 strips: G leaves in two passes through the 64 KiB staging area, pass
+// p holding the MFMA column blocks ni = 2 p, 2 p + 1 of every wave: 32 tokens
+// per wave column, (kWaves / 2) x 32 = 128 tokens, as 128 rows of 512 bytes
+// whose 16-byte chunks are XOR-swizzled by the row, so that neither the
 // MFMA-layout writes nor the row reads pile onto a few banks.  Every wave
 // computes its part of a pass straight into staging (per element one FMA,
 // one exp2 and half a pack: the token's |scale| is folded into the exponent,
@@ -242,18 +244,19 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
 __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& acc, int64_t m0,
                                               int64_t n0, char* lds) {
   constexpr int kRowBytes = kTile * 2;        // 256 bf16 vocabulary columns
-  constexpr int kPassTok = kWaves / 2 * 32;   // tokens per pass: one 32-column block per wave column
+  constexpr int kNiPass = 2;                  // column blocks per wave per pass
+  constexpr int kPassTok = kWaves / 2 * kNiPass * kMfma;  // 128 tokens per pass
   static_assert(kPassTok * kRowBytes <= kStagingBytes, "staging fits in LDS");
+  static_assert(kNI % kNiPass == 0, "whole passes");
   const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int half = lane >> 5;
   const int64_t vrow0 = m0 + wm * kWaveM;
   const bool full = vrow0 + kWaveM <= a.v_len;  // no strip rows past v_len in this wave
   // strip rows of this wave below v_len (only used when !full, then < kWaveM)
   const int rows_left = full ? kWaveM : (int)max<int64_t>(a.v_len - vrow0, 0);
-  const int r_lane = (lane >> 5) * 4;  // acc_row(mi, e, lane) - acc_row(mi, e, 0)
+  const int r_lane = (lane >> 4) * 4;  // acc_row(mi, e, lane) - acc_row(mi, e, 0)
   const float scale_all = a.ctrl->grad_scale;
   const float abs_scale = fabsf(scale_all);
   const uint32_t sign = scale_all < 0.f ? 0x80008000u : 0u;
@@ -264,7 +267,7 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
   bool any_hit[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
-    const int64_t tok = n0 + wn * kWaveN + ni * 32 + (lane & 31);
+    const int64_t tok = n0 + wn * kWaveN + ni * kMfma + (lane & 15);
     const bool tok_ok = tok < a.N;
     const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
     const bool valid = t != a.ignore_index;
@@ -282,44 +285,48 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
   const __amdgpu_buffer_rsrc_t gbuf =
       make_buffer(a.g_strip + n0 * a.ldg + m0, (a.N - n0) * row_bytes - m0 * 2);
 #pragma unroll
-  for (int ni = 0; ni < kNI; ++ni) {
+  for (int pass = 0; pass < kNI / kNiPass; ++pass) {
     block_barrier();  // staging free: the previous pass (or tile) is done with it
-    {
-      float v[64];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+    for (int nj = 0; nj < kNiPass; ++nj) {
+      const int ni = pass * kNiPass + nj;
+      float v[4 * kMI];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          v[mi * 16 + e] = fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, c[ni]));
+      for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[mi * 4 + e] = fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, c[ni]));
       // Row tests against the lane's row offset: acc_row(mi, e, lane) =
       // acc_row(mi, e, 0) + r_lane, so each compares one VGPR with a constant.
       if (!full) {
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            v[mi * 16 + e] = r_lane < rows_left - acc_row(mi, e, 0) ? v[mi * 16 + e] : 0.f;
+          for (int e = 0; e < 4; ++e)
+            v[mi * 4 + e] = r_lane < rows_left - acc_row(mi, e, 0) ? v[mi * 4 + e] : 0.f;
       }
       if (any_hit[ni]) {
         const int d = tl[ni] - r_lane;  // the target's row minus the lane's offset
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            v[mi * 16 + e] = d == acc_row(mi, e, 0) ? v[mi * 16 + e] - abs_scale : v[mi * 16 + e];
+          for (int e = 0; e < 4; ++e)
+            v[mi * 4 + e] = d == acc_row(mi, e, 0) ? v[mi * 4 + e] - abs_scale : v[mi * 4 + e];
       }
-      const int row = wn * 32 + (lane & 31);  // staging row of this lane's token
-      char* lrow = lds + row * kRowBytes + half * 8;
+      // staging row of this lane's token: wave column wn, block nj, lane % 16
+      const int row = wn * kNiPass * kMfma + nj * kMfma + (lane & 15);
+      // its 4 rows acc_row(mi, 0..3, lane) are columns wm*128 + mi*16 + r_lane:
+      // byte 2 (...) = 16-byte chunk wm*16 + 2 mi + (lane >> 5), half (lane >> 4) & 1
+      char* lrow = lds + row * kRowBytes + ((lane >> 4) & 1) * 8;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float* w = &v[mi * 16 + 4 * q];
-          const u32x2_t pk = GPack<__bf16>::pack(w[0], w[1], w[2], w[3]);
-          const int chunk = wm * 16 + mi * 4 + q;  // 16-byte chunk of columns
-          *reinterpret_cast<u32x2_t*>(lrow + ((chunk ^ (row & 31)) * 16)) =
-              u32x2_t{pk[0] ^ sign, pk[1] ^ sign};
-        }
+      for (int mi = 0; mi < kMI; ++mi) {
+        const float* w = &v[mi * 4];
+        const u32x2_t pk = GPack<__bf16>::pack(w[0], w[1], w[2], w[3]);
+        const int chunk = wm * 16 + mi * 2 + (lane >> 5);
+        *reinterpret_cast<u32x2_t*>(lrow + ((chunk ^ (row & 31)) * 16)) =
+            u32x2_t{pk[0] ^ sign, pk[1] ^ sign};
+      }
+      sched_fence();  // one column block at a time: its 32 values, then the next
     }
     block_barrier();
     const int run = tid & 31;  // 16-byte run of a row
@@ -328,8 +335,8 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
       const int row = (tid >> 5) + (kThreads / 32) * i;
       const u32x4_t val =
           *reinterpret_cast<const u32x4_t*>(lds + row * kRowBytes + ((run ^ (row & 31)) * 16));
-      // staging row -> token: wave column row / 32, column block ni, lane row % 32
-      const int tok = (row >> 5) * kWaveN + ni * 32 + (row & 31);
+      // staging row -> token: wave column row / 32, block row / 16 % 2, lane row % 16
+      const int tok = (row >> 5) * kWaveN + (pass * kNiPass + ((row >> 4) & 1)) * kMfma + (row & 15);
       const uint32_t off = (uint32_t)(tok * row_bytes) + run * 16;
       __builtin_amdgcn_raw_buffer_store_b128(val, gbuf, off, 0, 0);
     }
@@ -353,11 +360,11 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
 // Plain fp32-output GEMM tile: C[m, n] (+)= sum_k A[m, k] B[n, k].
 //
 // The epilogue goes through the LDS staging area in four passes of 64 rows
-// (1 KiB each, unpadded: the 16-byte chunk index is XOR-swizzled by the row,
-// so the two rows of an MFMA-layout write never share banks): the waves that
-// hold those rows write them, then all threads move whole 16-byte runs of
-// each row, so that every wave reads and writes 1 KiB of one row of C per
-// instruction.  With Accum a pass issues half of its loads of C before
+// (1 KiB each, unpadded: the 16-byte chunk index is XOR-swizzled by row bits
+// 2..3, so the four rows of an MFMA-layout write never share banks): the
+// waves that hold those rows write them, then all threads move whole 16-byte
+// runs of each row, so that every wave reads and writes 1 KiB of one row of C
+// per instruction.  With Accum a pass issues half of its loads of C before
 // the staging writes, so that their latency hides behind them.
 // ---------------------------------------------------------------------------
 constexpr int kEpiRows = 64;                        // rows of C per pass
@@ -366,7 +373,7 @@ static_assert(kEpiRows * kEpiRowBytes <= kStagingBytes, "epilogue staging fits i
 
 // Byte offset in the staging area of 16-byte chunk `chunk` of row `row`.
 __device__ __forceinline__ int epi_offset(int row, int chunk) {
-  return row * kEpiRowBytes + ((chunk ^ (((row >> 2) & 1) << 3)) * 16);
+  return row * kEpiRowBytes + ((chunk ^ (((row >> 2) & 3) << 2)) * 16);
 }
 
 template <typename T, bool Accum>
@@ -401,16 +408,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs<T>& g, Acc& acc, in
     }
     block_barrier();  // staging free: the previous pass (or tile) is done with it
     if (wm == pass / 2) {
-      // rows 64 (pass % 2) .. +64 of this wave's 128 = sub-tiles mi = 2 (pass % 2) + {0, 1}
+      // rows 64 (pass % 2) .. +64 of this wave's 128 = sub-tiles mi = 4 (pass % 2) + h
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int mi = 2 * (pass % 2) + h;
+      for (int h = 0; h < kEpiRows / kMfma; ++h) {
+        const int mi = (kEpiRows / kMfma) * (pass % 2) + h;
 #pragma unroll
         for (int ni = 0; ni < kNI; ++ni) {
-          const int col = wn * kWaveN + ni * 32 + (lane & 31);
+          const int col = wn * kWaveN + ni * kMfma + (lane & 15);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int row = h * 32 + acc_row(0, e, lane);
+          for (int e = 0; e < 4; ++e) {
+            const int row = h * kMfma + acc_row(0, e, lane);
             *reinterpret_cast<float*>(lds + epi_offset(row, col >> 2) + (col & 3) * 4) =
                 acc.c[mi][ni][e];
           }

@@ -1,8 +1,9 @@
 // tile_engine.h - one 256x256 MFMA tile of C = A . B^T on gfx950 (CDNA4).
 //
 // A block of 512 threads (eight wave64s in a 2x4 grid, two per SIMD, each
-// owning a 128x64 sub-tile of fp32 accumulators) walks K in stages of 64
-// bytes per row (32 bf16 or 16 f32 elements).  Two waves per SIMD let one
+// owning a 128x64 sub-tile of fp32 accumulators as 8 x 4 MFMA tiles of
+// 16 x 16) walks K in stages of 64 bytes per row (32 bf16 or 16 f32
+// elements).  Two waves per SIMD let one
 // wave's MFMAs run while the other waits on an LDS read or on the texture
 // unit; LDS read bandwidth (about 240 B/clk per CU with eight waves, half
 // that with four) covers the 1.5x fragment reads this layout costs.  Stages
@@ -15,8 +16,11 @@
 // burst stall every wave's MFMA issue at once; spread out, they hide behind
 // the MFMAs.  The lead given by the ring is what lets them be spread.
 // Fragments are read back from LDS as 16-byte K-runs that feed
-// v_mfma_f32_32x32x16_bf16 (bf16) or four v_mfma_f32_32x32x2_f32 (f32), one
-// k step ahead of their MFMAs.
+// v_mfma_f32_16x16x32_bf16 (bf16: one MFMA takes a whole stage's K) or four
+// v_mfma_f32_16x16x4_f32 (f32), half a stage ahead of their MFMAs.  Under
+// the part's power limit the 16x16x32 form delivers more FLOP per joule than
+// 32x32x16: it reads and writes a quarter of the accumulator bytes per MFMA
+// for half the FLOP.
 //
 // Operands may be stored K-contiguous (element (mn, k) at row mn, column k)
 // or MN-contiguous (element (mn, k) at row k, column mn):
@@ -26,8 +30,8 @@
 //    index swizzled by the k-row) and read with ds_read_b64_tr_b16, which
 //    hands each lane four K values of one column; two such reads make a
 //    fragment.  f32 stages (16 k-rows of 1 KiB) are read one float at a time.
-// Both swizzles keep every fragment read free of LDS bank conflicts for 32
-// or 64 four-byte banks.
+// Both bf16 swizzles keep every fragment read free of LDS bank conflicts
+// (64 four-byte banks, 256 bytes per cycle).
 //
 // Loads go through buffer resources whose record count ends at the last
 // valid row, so rows past the operand's extent read as zeros and nothing is
@@ -40,7 +44,6 @@
 namespace lce {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
@@ -50,10 +53,11 @@ constexpr int kTile = 256;                 // block tile along M and along N
 constexpr int kWaves = 8;                  // waves per block, 2 along M x kWaves / 2 along N
 constexpr int kWaveM = 128;                // wave sub-tile along M
 constexpr int kWaveN = kTile / (kWaves / 2);  // wave sub-tile along N
-constexpr int kNI = kWaveN / 32;           // 32-column MFMA tiles of a wave along N
+constexpr int kMfma = 16;                  // MFMA tile edge (16 x 16 outputs)
+constexpr int kMI = kWaveM / kMfma;        // MFMA tiles of a wave along M
+constexpr int kNI = kWaveN / kMfma;        // MFMA tiles of a wave along N
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStageRowBytes = 64;         // K bytes per row per stage
-constexpr int kSteps = kStageRowBytes / 32;   // k16 (bf16) / k8 (f32) steps per stage
+constexpr int kStageRowBytes = 64;         // K bytes per row per stage (one 16x16x32 bf16 MFMA)
 constexpr int kChunks = kStageRowBytes / 16;  // 16-byte chunks per row per stage
 constexpr int kOperandBytes = kTile * kStageRowBytes;   // per operand per stage
 constexpr int kStageBytes = 2 * kOperandBytes;          // A and B
@@ -63,7 +67,7 @@ constexpr int kStagingBytes = 64 * 1024;   // epilogue staging, after the ring
 constexpr int kLdsBytes = kRingBytes + kStagingBytes;
 constexpr int kCopiesPerWave = kOperandBytes / 1024 / kWaves;  // 1 KiB per wave-wide copy
 constexpr int kRowsPerCopy = 1024 / kStageRowBytes;       // K-contiguous rows per copy
-static_assert(kStageRowBytes == 64 && kSteps == 2, "stages of two 16-deep k steps");
+static_assert(kStageRowBytes == 64 && kChunks == 4, "a stage is one 16-byte run per lane group");
 static_assert(kStages >= 3 && kLdsBytes <= 160 * 1024, "ring and staging fit in LDS");
 constexpr uint32_t kOutOfRange = 0x80000000u;           // voffset that reads zeros
 constexpr int kRsrcWord3 = 0x00020000;                  // raw buffer, gfx9 family
@@ -74,8 +78,12 @@ __device__ __forceinline__ int swz_k(int r) {
   return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
 }
 // Swizzle of an MN-contiguous bf16 stage: physical chunk = chunk ^ swz_mn(k-row).
+// A transposed fragment read covers, per 32 lanes, the same two chunks of the
+// k-rows {0..3, 8..11} (+ 4, + 16): XOR-ing the 32-byte window index with
+// (k & 3) | ((k >> 3) & 1) << 2 puts those eight k-rows in eight different
+// 32-byte windows of the 256-byte bank period.
 __device__ __forceinline__ int swz_mn(int k) {
-  return ((k & 1) ? 10 : 0) ^ ((k & 2) ? 4 : 0);
+  return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
 }
 
 // Record count of a descriptor for `bytes` bytes, capped at 2^31 so that the
@@ -148,7 +156,7 @@ struct Side<T, true> {
   uint32_t voff[kCopiesPerWave];
   uint32_t kbyte;        // byte column of this lane's logical chunk
   int64_t k_ext_bytes;
-  uint32_t frag_off[kSteps];  // per k step: byte offset of this lane's fragment (mi = 0)
+  uint32_t frag_off;     // byte offset of this lane's fragment (mi = 0)
 
   // Point the copies at the tile whose first row is mn0.
   __device__ __forceinline__ void retarget(const Operand<T>& op, int64_t mn0) {
@@ -167,12 +175,11 @@ struct Side<T, true> {
       const int row = kRowsPerCopy * (kCopiesPerWave * wave + i) + rsub;
       voff[i] = (uint32_t)(row * row_bytes) + kbyte;
     }
-    const int frow = sub0 + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < kSteps; ++j) {
-      const int ch = 2 * j + (lane >> 5);
-      frag_off[j] = (uint32_t)(frow * kStageRowBytes + ((ch ^ swz_k(frow)) * 16));
-    }
+    // fragment: row lane % 16 of the 16-row sub-tile, logical chunk lane / 16
+    // (K elements 8 (lane / 16) .. + 8 of bf16, 4 (lane / 16) .. + 4 of f32);
+    // swz_k sees only row bits 1..3, which sub0 and the sub-tile leave alone
+    const int frow = sub0 + (lane & 15);
+    frag_off = (uint32_t)(frow * kStageRowBytes + (((lane >> 4) ^ swz_k(frow)) * 16));
   }
   __device__ __forceinline__ void init(const Operand<T>& op, int64_t mn0, int wave, int lane,
                                        int sub0) {
@@ -193,9 +200,9 @@ struct Side<T, true> {
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
   }
-  // Fragment of sub-tile mi for k step j of the stage at src.
-  __device__ __forceinline__ u32x4_t frag(const char* src, int mi, int j) const {
-    return *reinterpret_cast<const u32x4_t*>(src + frag_off[j] + mi * 32 * kStageRowBytes);
+  // Fragment of 16-row sub-tile mi of the stage at src.
+  __device__ __forceinline__ u32x4_t frag(const char* src, int mi) const {
+    return *reinterpret_cast<const u32x4_t*>(src + frag_off + mi * kMfma * kStageRowBytes);
   }
 };
 
@@ -209,7 +216,7 @@ struct Side<__bf16, false> {
   int64_t k_ext;
   int64_t mn0_bytes;
   uint32_t voff[kCopiesPerWave];
-  uint32_t frag_off[4];   // per mi: byte offset of this lane's first transposed read
+  uint32_t frag_off[kMI];  // per mi: byte offset of this lane's first transposed read
 
   __device__ __forceinline__ void retarget(const Operand<__bf16>& op, int64_t mn0) {
     base = reinterpret_cast<const char*>(op.base + mn0);
@@ -232,15 +239,16 @@ struct Side<__bf16, false> {
     }
     // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
     // i % 4 of the 8-byte runs addressed by lanes i / 4 + 4 r (r = 0..3).
-    // Lane jj of group g addresses k-row 8 (g / 2) + jj / 4 (+ 4 for the second
-    // read, + 16 j for k16 step j) and the 4 columns 16 (g % 2) + 4 (jj % 4)
-    // of its 32-column sub-tile, so lane i of the group gets 4 K values of
-    // column 16 (g % 2) + i, as the MFMA operand expects.
+    // Lane jj of group g addresses k-row 8 g + jj / 4 (+ 4 for the second
+    // read) and the 4 columns 4 (jj % 4) of its 16-column sub-tile, so lane i
+    // of the group gets K values 8 g .. 8 g + 7 of column i, as the MFMA
+    // operand expects.  swz_mn(kr + 4) == swz_mn(kr), so one offset serves
+    // both reads.
     const int g = lane >> 4, jj = lane & 15;
-    const int kr = 8 * (g >> 1) + (jj >> 2);  // swz_mn depends on kr % 4 only
+    const int kr = 8 * g + (jj >> 2);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int col = sub0 + mi * 32 + 16 * (g & 1) + 4 * (jj & 3);
+    for (int mi = 0; mi < kMI; ++mi) {
+      const int col = sub0 + mi * kMfma + 4 * (jj & 3);
       const int c = (col >> 3) ^ swz_mn(kr);
       frag_off[mi] = (uint32_t)(kr * 512 + c * 16 + (col & 7) * 2);
     }
@@ -256,8 +264,8 @@ struct Side<__bf16, false> {
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
   }
-  __device__ __forceinline__ u32x4_t frag(const char* src, int mi, int j) const {
-    const char* p = src + frag_off[mi] + j * 16 * 512;
+  __device__ __forceinline__ u32x4_t frag(const char* src, int mi) const {
+    const char* p = src + frag_off[mi];
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
     const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p + 4 * 512));
     const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
@@ -296,7 +304,8 @@ struct Side<float, false> {
       const int kr = kCopiesPerWave * wave + i;
       voff[i] = (uint32_t)(kr * row_bytes + lane * 16);
     }
-    frag_off = (uint32_t)((sub0 + (lane & 31)) * 4 + (lane >> 5) * 4 * 1024);
+    // column lane % 16 of the sub-tile, k-rows 4 (lane / 16) .. + 4
+    frag_off = (uint32_t)((sub0 + (lane & 15)) * 4 + (lane >> 4) * 4 * 1024);
   }
   __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
                                           int i) const {
@@ -308,9 +317,9 @@ struct Side<float, false> {
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
   }
-  // k step j covers k-rows 8 j .. 8 j + 7: lane half h takes rows 8 j + 4 h + q.
-  __device__ __forceinline__ u32x4_t frag(const char* src, int mi, int j) const {
-    const char* p = src + frag_off + mi * 32 * 4 + j * 8 * 1024;
+  // Lane group h (= lane / 16) takes k-rows 4 h + q, q = 0..3.
+  __device__ __forceinline__ u32x4_t frag(const char* src, int mi) const {
+    const char* p = src + frag_off + mi * kMfma * 4;
     u32x4_t v;
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const uint32_t*>(p + q * 1024);
@@ -323,61 +332,59 @@ struct Side<float, false> {
 // ---------------------------------------------------------------------------
 template <typename T> struct Mfma;
 
+// A and B use the same K assignment (lane group h = lane / 16 holds K
+// elements 8 h .. 8 h + 7 of a bf16 stage), so every product pairs equal K.
 template <>
 struct Mfma<__bf16> {
-  __device__ __forceinline__ static f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+  __device__ __forceinline__ static f32x4_t run(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
 };
 
 template <>
 struct Mfma<float> {
-  // The four floats of a fragment are four successive K steps of 32x32x2; the
-  // two lane halves supply the two K values of each step.  A and B use the
-  // same assignment, so every product pairs equal K.  Each element is copied
-  // to a scalar before the bit cast: a bit cast of a vector-element lvalue
-  // reads element 0 whatever the index.
-  __device__ __forceinline__ static f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
+  // Float q of lane group h's fragment is K element 4 h + q of the stage;
+  // MFMA q of the four takes those (one K value per lane group), for A and B
+  // alike.  Each element is copied to a scalar before the bit cast: a bit
+  // cast of a vector-element lvalue reads element 0 whatever the index.
+  __device__ __forceinline__ static f32x4_t run(u32x4_t a, u32x4_t b, f32x4_t c) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t ua = a[q];
       const uint32_t ub = b[q];
-      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, ua),
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, ua),
                                                __builtin_bit_cast(float, ub), c, 0, 0, 0);
     }
     return c;
   }
 };
 
-// Accumulators of one wave: 4 x kNI MFMA tiles of 32 x 32.
+// Accumulators of one wave: kMI x kNI MFMA tiles of 16 x 16.
 // Element (mi, ni, e) of lane l sits at tile row
-//   wm*kWaveM + mi*32 + (e/4)*8 + (l/32)*4 + e%4   and column  wn*kWaveN + ni*32 + l%32.
+//   wm*kWaveM + mi*16 + (l/16)*4 + e   and column  wn*kWaveN + ni*16 + l%16.
 struct Acc {
-  f32x16_t c[4][kNI];
+  f32x4_t c[kMI][kNI];
 };
 
 __device__ __forceinline__ int acc_row(int mi, int e, int lane) {
-  return mi * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+  return mi * kMfma + (lane >> 4) * 4 + e;
 }
 
+// Fragments of one stage: a[mi] for the kMI sub-tiles of A, b[ni] for the kNI
+// of B.  A stage's MFMAs run in two halves (sub-tiles mi < kMI / 2, then the
+// rest), so each register is refilled from the next stage as soon as its
+// last MFMA of this stage has issued.
 template <typename T, bool AK, bool BK>
 struct Frags {
-  static constexpr int kReads = 4 + kNI;
-  u32x4_t a[4], b[kNI];
-  __device__ __forceinline__ void read(const Side<T, AK>& sa, const Side<T, BK>& sb,
-                                       const char* stage, int j) {
+  u32x4_t a[kMI], b[kNI];
+  // What the first half of a stage needs: a[0 .. kMI / 2) and all of b.
+  __device__ __forceinline__ void read_first(const Side<T, AK>& sa, const Side<T, BK>& sb,
+                                             const char* stage) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = sa.frag(stage, i, j);
+    for (int i = 0; i < kMI / 2; ++i) a[i] = sa.frag(stage, i);
 #pragma unroll
-    for (int i = 0; i < kNI; ++i) b[i] = sb.frag(stage + kOperandBytes, i, j);
-  }
-  // Read r of kReads, in the order the MFMAs first use them: a0, all of b, a1..a3.
-  __device__ __forceinline__ void read_one(const Side<T, AK>& sa, const Side<T, BK>& sb,
-                                           const char* stage, int j, int r) {
-    if (r == 0) a[0] = sa.frag(stage, 0, j);
-    else if (r <= kNI) b[r - 1] = sb.frag(stage + kOperandBytes, r - 1, j);
-    else a[r - kNI] = sa.frag(stage, r - kNI, j);
+    for (int i = 0; i < kNI; ++i) b[i] = sb.frag(stage + kOperandBytes, i);
   }
 };
 
@@ -467,27 +474,37 @@ struct Cursor {
   }
 };
 
-// Half a stage: the 4 kNI MFMAs of one k step (fragments `use`), with the
-// 4 + kNI fragment reads of the next k step (into `fill`, step j of the stage
-// at src) after the first MFMAs, and, with Copy, the kNI copies of one
-// operand's current stage after MFMAs 1, 5, 9, ... (one copy per four MFMAs).  Spreading the copies keeps the
-// MFMA pipe fed while the texture unit works through them; issued in a burst,
-// they would hold every wave of the CU at once.
-template <bool Reads, bool Copy, typename T, bool AK, bool BK, typename C>
+// Half H of a stage: the MFMAs of sub-tiles mi in [H kMI / 2, (H + 1) kMI / 2)
+// for every ni, ni-major (so b[ni] sees its last MFMA of the stage early in
+// the second half), with the fragment reads that refill registers:
+//   H = 0: a[kMI / 2 ..) of this stage (src = this stage);
+//   H = 1: a[0 .. kMI / 2) and each b[ni], right after its last use, of the
+//          next stage (src = next stage);
+// and, with Copy, the kCopiesPerWave copies of one operand's current stage,
+// one after every eighth MFMA.  Spreading the copies keeps the MFMA pipe fed
+// while the texture unit works through them; issued in a burst, they would
+// hold every wave of the CU at once.
+template <int H, bool Reads, bool Copy, typename T, bool AK, bool BK, typename C>
 __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, BK>& sb,
-                                           const Frags<T, AK, BK>& use, Frags<T, AK, BK>& fill,
-                                           const char* src, int j, const C& cur, uint32_t lds0,
-                                           uint32_t off, int wave, int64_t tiles, Acc& acc) {
-  static_assert(kCopiesPerWave == kNI, "one copy per four MFMAs");
+                                           Frags<T, AK, BK>& f, const char* src, const C& cur,
+                                           uint32_t lds0, uint32_t off, int wave, int64_t tiles,
+                                           Acc& acc) {
+  constexpr int kHalf = kMI / 2;  // sub-tiles along M per half
+  static_assert(kHalf == 4 && kHalf * kNI == 8 * kCopiesPerWave, "one copy per eight MFMAs");
 #pragma unroll
-  for (int t = 0; t < 4 * kNI; ++t) {
-    acc.c[t / kNI][t % kNI] =
-        Mfma<T>::run(use.a[t / kNI], use.b[t % kNI], acc.c[t / kNI][t % kNI]);
+  for (int t = 0; t < kHalf * kNI; ++t) {
+    const int ni = t / kHalf, mi = H * kHalf + t % kHalf;
+    acc.c[mi][ni] = Mfma<T>::run(f.a[mi], f.b[ni], acc.c[mi][ni]);
     if constexpr (Reads) {
-      if (t < Frags<T, AK, BK>::kReads) fill.read_one(sa, sb, src, j, t);
+      if constexpr (H == 0) {
+        if (t < kHalf) f.a[kHalf + t] = sa.frag(src, kHalf + t);
+      } else {
+        if (t % kHalf == kHalf - 1) f.b[ni] = sb.frag(src + kOperandBytes, ni);
+        else if (t < 5) f.a[t < 3 ? t : t - 1] = sa.frag(src, t < 3 ? t : t - 1);
+      }
     }
     if constexpr (Copy) {
-      if ((t & 3) == 1) cur.copy_one(lds0, off, wave, tiles, t >> 2);
+      if ((t & 7) == 1) cur.copy_one(lds0, off, wave, tiles, t >> 3);
     }
     // The order above is pinned where an operand is read with transposing
     // reads (measured faster); with both operands K-contiguous the compiler's
@@ -501,16 +518,18 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
 // and kStagingBytes of LDS after the ring free for the epilogue.
 //
 // All tiles of the block form one stream of stages (a tile is nk stages of
-// two k steps; stage s lives in ring buffer s % kStages).  The copies run
+// one MFMA K step; stage s lives in ring buffer s % kStages).  The copies run
 // ahead of the MFMAs by the depth of the ring, across tile boundaries, so the
 // first stages of the next tile land while a tile's epilogue runs.  With the
-// MFMAs at stage s (step 0 in fragment set f0, step 1 in f1):
-//   half A: MFMAs of step 0, reads of step 1, B copies of stage s + kStages - 1
-//           (into the buffer freed at the previous barrier);
+// MFMAs at stage s:
+//   half A: MFMAs of sub-tiles mi < kMI / 2, reads of the other a[] of stage
+//           s (its last reads), B copies of stage s + kStages - 1 (into the
+//           buffer freed at the previous barrier);
 //   wait until stage s + 1 has landed and this wave's reads are done; barrier
 //           (every wave is past its last read of buffer s % kStages);
-//   half B: MFMAs of step 1, reads of step 0 of stage s + 1, A copies of stage
-//           s + kStages (into buffer s % kStages).
+//   half B: MFMAs of sub-tiles mi >= kMI / 2, reads of a[0 .. kMI / 2) and b[]
+//           of stage s + 1, A copies of stage s + kStages (into buffer
+//           s % kStages).
 // Every stage issues one stage of copies, so the waits are constants; past the
 // block's last stage the copies are dead (they read zeros into buffers that
 // are not read again).  The last stage of a tile is peeled off, so the loop
@@ -530,7 +549,6 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
 template <typename T, bool AK, bool BK, typename Epi>
 __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int64_t k_len,
                                           const TileGrid& grid, char* lds, Epi&& epi) {
-  static_assert(kSteps == 2, "pipeline written for two k steps per stage");
   constexpr int64_t kStageK = kStageRowBytes / sizeof(T);
   constexpr int kPerStage = 2 * kCopiesPerWave;  // copies per wave per stage
   const int tid = threadIdx.x;
@@ -571,7 +589,7 @@ __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>&
   block_barrier();
 
   Acc acc;
-  Frags<T, AK, BK> f0, f1;
+  Frags<T, AK, BK> f;
   uint32_t buf = 0;  // ring buffer of the stage the MFMAs are at
   for (int64_t i = 0; i < tiles; ++i) {
     {
@@ -581,31 +599,31 @@ __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>&
       cb.side.init_lanes(B, wave, l, wn * kWaveN);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < kMI; ++r)
 #pragma unroll
-      for (int c = 0; c < kNI; ++c) acc.c[r][c] = f32x16_t{};
-    f0.read(sa, sb, lds + buf * kStageBytes, 0);
+      for (int c = 0; c < kNI; ++c) acc.c[r][c] = f32x4_t{};
+    f.read_first(sa, sb, lds + buf * kStageBytes);
     sched_fence();
     for (int64_t kt = 0; kt + 1 < nk; ++kt) {
       const uint32_t next = buf + 1 == kStages ? 0u : buf + 1;
-      half_stage<true, true>(sa, sb, f0, f1, lds + buf * kStageBytes, 1, cb, lds0,
-                             kOperandBytes, wave, tiles, acc);
+      half_stage<0, true, true>(sa, sb, f, lds + buf * kStageBytes, cb, lds0, kOperandBytes,
+                                wave, tiles, acc);
       cb.advance(B, nk, next_n0);
       wait_copies<(kStages - 2) * kPerStage>();
       block_barrier();
-      half_stage<true, true>(sa, sb, f1, f0, lds + next * kStageBytes, 0, ca, lds0, 0, wave,
-                             tiles, acc);
+      half_stage<1, true, true>(sa, sb, f, lds + next * kStageBytes, ca, lds0, 0, wave, tiles,
+                                acc);
       ca.advance(A, nk, next_m0);
       buf = next;
     }
     {
       const uint32_t next = buf + 1 == kStages ? 0u : buf + 1;
-      half_stage<true, true>(sa, sb, f0, f1, lds + buf * kStageBytes, 1, cb, lds0,
-                             kOperandBytes, wave, tiles, acc);
+      half_stage<0, true, true>(sa, sb, f, lds + buf * kStageBytes, cb, lds0, kOperandBytes,
+                                wave, tiles, acc);
       cb.advance(B, nk, next_n0);
       wait_copies<(kStages - 2) * kPerStage>();
       block_barrier();
-      half_stage<false, true>(sa, sb, f1, f0, lds, 0, ca, lds0, 0, wave, tiles, acc);
+      half_stage<1, false, true>(sa, sb, f, lds, ca, lds0, 0, wave, tiles, acc);
       ca.advance(A, nk, next_m0);
       buf = next;
     }
