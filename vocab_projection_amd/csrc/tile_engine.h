@@ -145,18 +145,31 @@ struct Operand {
 // ---------------------------------------------------------------------------
 // Stage copies (global -> LDS) and fragment reads (LDS -> registers).
 // ---------------------------------------------------------------------------
-template <typename T, bool KContig> struct Side;
+// Operand layouts in LDS: MN-contiguous, K-contiguous row-major, and
+// K-contiguous with the split sub-tile placement below.
+enum : int { kMN = 0, kKRow = 1, kKSplit = 2 };
+template <typename T, int L> struct Side;
 
-// K-contiguous operand.  Copy i of wave w covers rows kRowsPerCopy (c w + i)
-// .. + kRowsPerCopy (c = kCopiesPerWave): lane l fills physical chunk
-// l % kChunks of row kRowsPerCopy (c w + i) + l / kChunks.
-template <typename T>
-struct Side<T, true> {
+// K-contiguous operand.  A stage is 16 blocks of 1 KiB, each 16 row slots of
+// 64 bytes (four 16-byte chunks, chunk index XOR-swizzled by swz_k(slot)).
+// Row-major (kKRow): block b, slot s holds row 16 b + s.  Split (kKSplit):
+// each 32-row group of the tile (two 16-row MFMA sub-tiles h = 0, 1) takes
+// two blocks b = 0, 1, and block b, slot 8 h + s holds row 16 h + 8 b + s of
+// the group.  A fragment read (lane l: row l % 16 of a sub-tile, chunk
+// l / 16) then takes 8 slots from each of two blocks, which measured free of
+// LDS bank conflicts, while 16 slots of one block cost a 2-way conflict on
+// every read.  The split placement pays where both operands are
+// K-contiguous (the strip kernels, 1% faster); with a transposed operand
+// beside it (dH) the row-major one measured 3% faster.  Copy i of wave w
+// fills block c = c w + i (c = kCopiesPerWave): lane l reads physical chunk
+// l % kChunks of the row in slot l / kChunks, 64 contiguous bytes per 4 lanes.
+template <typename T, bool Split>
+struct SideK {
   u32x4_t rsrc;
   uint32_t voff[kCopiesPerWave];
   uint32_t kbyte;        // byte column of this lane's logical chunk
   int64_t k_ext_bytes;
-  uint32_t frag_off;     // byte offset of this lane's fragment (mi = 0)
+  uint32_t frag_off[2];  // byte offset of this lane's fragment, even and odd sub-tile of pair 0
 
   // Point the copies at the tile whose first row is mn0.
   __device__ __forceinline__ void retarget(const Operand<T>& op, int64_t mn0) {
@@ -166,20 +179,27 @@ struct Side<T, true> {
   __device__ __forceinline__ void init_lanes(const Operand<T>& op, int wave, int lane, int sub0) {
     const int64_t row_bytes = op.ld * (int64_t)sizeof(T);
     k_ext_bytes = op.k_ext * (int64_t)sizeof(T);
-    const int rsub = lane / kChunks;  // row within a copy
-    // swz_k depends on row bits 1..3, which the lane fixes (16 rows per copy)
-    static_assert(kRowsPerCopy == 16, "one swizzle per lane");
-    kbyte = (uint32_t)(((lane % kChunks) ^ swz_k(rsub)) * 16);
+    const int slot = lane / kChunks;  // row slot within a copy's block
+    static_assert(kRowsPerCopy == 16, "a copy fills one block of 16 slots");
+    kbyte = (uint32_t)(((lane % kChunks) ^ swz_k(slot)) * 16);
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) {
-      const int row = kRowsPerCopy * (kCopiesPerWave * wave + i) + rsub;
+      const int c = kCopiesPerWave * wave + i;  // block
+      const int row = Split ? 32 * (c >> 1) + 16 * (slot >> 3) + 8 * (c & 1) + (slot & 7)
+                            : 16 * c + slot;
       voff[i] = (uint32_t)(row * row_bytes) + kbyte;
     }
-    // fragment: row lane % 16 of the 16-row sub-tile, logical chunk lane / 16
-    // (K elements 8 (lane / 16) .. + 8 of bf16, 4 (lane / 16) .. + 4 of f32);
-    // swz_k sees only row bits 1..3, which sub0 and the sub-tile leave alone
-    const int frow = sub0 + (lane & 15);
-    frag_off = (uint32_t)(frow * kStageRowBytes + (((lane >> 4) ^ swz_k(frow)) * 16));
+    // fragment: row j = lane % 16 of the sub-tile, logical chunk lane / 16
+    // (K elements 8 (lane / 16) .. + 8 of bf16, 4 (lane / 16) .. + 4 of f32).
+    // Split: sub-tile h of a pair has row j in block j / 8, slot 8 h + j % 8.
+    // sub0 is a multiple of 32 rows.
+    const int j = lane & 15;
+#pragma unroll
+    for (int h = 0; h < (Split ? 2 : 1); ++h) {
+      const int fslot = Split ? 8 * h + (j & 7) : j;  // slot from the pair's first block
+      frag_off[h] = (uint32_t)(sub0 * kStageRowBytes + (Split ? (j >> 3) * 1024 : 0) +
+                               fslot * kStageRowBytes + (((lane >> 4) ^ swz_k(fslot)) * 16));
+    }
   }
   __device__ __forceinline__ void init(const Operand<T>& op, int64_t mn0, int wave, int lane,
                                        int sub0) {
@@ -200,17 +220,25 @@ struct Side<T, true> {
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
   }
-  // Fragment of 16-row sub-tile mi of the stage at src.
+  // Fragment of 16-row sub-tile mi of the stage at src (pair mi / 2 is the
+  // 32-row group's 2 KiB).
   __device__ __forceinline__ u32x4_t frag(const char* src, int mi) const {
-    return *reinterpret_cast<const u32x4_t*>(src + frag_off + mi * kMfma * kStageRowBytes);
+    if constexpr (Split)
+      return *reinterpret_cast<const u32x4_t*>(src + frag_off[mi & 1] +
+                                               (mi >> 1) * 2 * kMfma * kStageRowBytes);
+    else
+      return *reinterpret_cast<const u32x4_t*>(src + frag_off[0] + mi * kMfma * kStageRowBytes);
   }
 };
+
+template <typename T> struct Side<T, kKRow> : SideK<T, false> {};
+template <typename T> struct Side<T, kKSplit> : SideK<T, true> {};
 
 // MN-contiguous bf16 operand: a stage is kStageRowBytes / 2 k-rows x 256 mn.
 // Copy i of wave w covers k-rows 2 (c w + i) and +1 (c = kCopiesPerWave); lane
 // l fills physical chunk l % 32 of k-row 2 (c w + i) + l / 32.
 template <>
-struct Side<__bf16, false> {
+struct Side<__bf16, kMN> {
   const char* base;       // element (mn0, k = 0)
   int64_t row_bytes;
   int64_t k_ext;
@@ -278,7 +306,7 @@ struct Side<__bf16, false> {
 // floats (1 KiB), one k-row per copy, no swizzle; fragments are read one float
 // at a time.
 template <>
-struct Side<float, false> {
+struct Side<float, kMN> {
   const char* base;
   int64_t row_bytes;
   int64_t k_ext;
@@ -375,7 +403,7 @@ __device__ __forceinline__ int acc_row(int mi, int e, int lane) {
 // of B.  A stage's MFMAs run in two halves (sub-tiles mi < kMI / 2, then the
 // rest), so each register is refilled from the next stage as soon as its
 // last MFMA of this stage has issued.
-template <typename T, bool AK, bool BK>
+template <typename T, int AK, int BK>
 struct Frags {
   u32x4_t a[kMI], b[kNI];
   // What the first half of a stage needs: a[0 .. kMI / 2) and all of b.
@@ -448,7 +476,7 @@ struct TileGrid {
 
 // Copies of one operand for a stream of stages that runs across this block's
 // tiles: the stage `kt` of tile `ti`, in ring buffer `buf`.
-template <typename T, bool KC>
+template <typename T, int KC>
 struct Cursor {
   Side<T, KC> side;
   int64_t kt, ti;
@@ -484,7 +512,7 @@ struct Cursor {
 // one after every eighth MFMA.  Spreading the copies keeps the MFMA pipe fed
 // while the texture unit works through them; issued in a burst, they would
 // hold every wave of the CU at once.
-template <int H, bool Reads, bool Copy, typename T, bool AK, bool BK, typename C>
+template <int H, bool Reads, bool Copy, typename T, int AK, int BK, typename C>
 __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, BK>& sb,
                                            Frags<T, AK, BK>& f, const char* src, const C& cur,
                                            uint32_t lds0, uint32_t off, int wave, int64_t tiles,
@@ -509,7 +537,7 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
     // The order above is pinned where an operand is read with transposing
     // reads (measured faster); with both operands K-contiguous the compiler's
     // own interleaving, with two waves per SIMD, measured faster still.
-    if constexpr (!(AK && BK)) sched_fence();
+    if constexpr (AK == kMN || BK == kMN) sched_fence();
   }
 }
 
@@ -568,12 +596,16 @@ __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>&
   next_n0 = n0;
   if (tiles > 1) grid.coords(1, &next_m0, &next_n0);
 
-  Cursor<T, AK> ca{{}, 0, 0, 0u};
-  Cursor<T, BK> cb{{}, 0, 0, 0u};
+  // K-contiguous operands take the split placement when both are (strip
+  // kernels), the row-major one beside a transposed operand.
+  constexpr int LA = !AK ? kMN : (BK ? kKSplit : kKRow);
+  constexpr int LB = !BK ? kMN : (AK ? kKSplit : kKRow);
+  Cursor<T, LA> ca{{}, 0, 0, 0u};
+  Cursor<T, LB> cb{{}, 0, 0, 0u};
   ca.side.init(A, m0, wave, lane, wm * kWaveM);
   cb.side.init(B, n0, wave, lane, wn * kWaveN);
-  const Side<T, AK>& sa = ca.side;  // fragment offsets do not depend on the tile
-  const Side<T, BK>& sb = cb.side;
+  const Side<T, LA>& sa = ca.side;  // fragment offsets do not depend on the tile
+  const Side<T, LB>& sb = cb.side;
 
   // Stages 0 .. kStages - 2 whole, and the A copies of stage kStages - 1.
 #pragma unroll
@@ -589,7 +621,7 @@ __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>&
   block_barrier();
 
   Acc acc;
-  Frags<T, AK, BK> f;
+  Frags<T, LA, LB> f;
   uint32_t buf = 0;  // ring buffer of the stage the MFMAs are at
   for (int64_t i = 0; i < tiles; ++i) {
     {
