@@ -509,16 +509,17 @@ struct Cursor {
 //   H = 1: a[0 .. kMI / 2) and each b[ni], right after its last use, of the
 //          next stage (src = next stage);
 // and, with Copy, the kCopiesPerWave copies of one operand's current stage,
-// one after every eighth MFMA.  Spreading the copies keeps the MFMA pipe fed
-// while the texture unit works through them; issued in a burst, they would
-// hold every wave of the CU at once.
+// one after MFMAs 0 and 4 (measured against other placements: after 1 and
+// 9 dH was 3% and dW 3% slower, the strip kernels the same).  Spreading the
+// copies keeps the MFMA pipe fed while the texture unit works through them;
+// issued in a burst, they would hold every wave of the CU at once.
 template <int H, bool Reads, bool Copy, typename T, int AK, int BK, typename C>
 __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, BK>& sb,
                                            Frags<T, AK, BK>& f, const char* src, const C& cur,
                                            uint32_t lds0, uint32_t off, int wave, int64_t tiles,
                                            Acc& acc) {
   constexpr int kHalf = kMI / 2;  // sub-tiles along M per half
-  static_assert(kHalf == 4 && kHalf * kNI == 8 * kCopiesPerWave, "one copy per eight MFMAs");
+  static_assert(kHalf == 4 && kNI == 4 && kCopiesPerWave == 2, "two copies per half stage");
 #pragma unroll
   for (int t = 0; t < kHalf * kNI; ++t) {
     const int ni = t / kHalf, mi = H * kHalf + t % kHalf;
@@ -532,7 +533,7 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
       }
     }
     if constexpr (Copy) {
-      if ((t & 7) == 1) cur.copy_one(lds0, off, wave, tiles, t >> 3);
+      if ((t & 3) == 0 && t < 8) cur.copy_one(lds0, off, wave, tiles, t >> 2);
     }
     // The order above is pinned where an operand is read with transposing
     // reads (measured faster); with both operands K-contiguous the compiler's
