@@ -145,10 +145,44 @@ struct Operand {
 // ---------------------------------------------------------------------------
 // Stage copies (global -> LDS) and fragment reads (LDS -> registers).
 // ---------------------------------------------------------------------------
-// Operand layouts in LDS: MN-contiguous, K-contiguous row-major, and
-// K-contiguous with the split sub-tile placement below.
-enum : int { kMN = 0, kKRow = 1, kKSplit = 2 };
+// Operand layouts in LDS: MN-contiguous (the copy descriptor recomputed per
+// stage, or followed by adds), K-contiguous row-major, and K-contiguous with
+// the split sub-tile placement below.
+enum : int { kMN = 0, kKRow = 1, kKSplit = 2, kMNStep = 3 };
+__host__ __device__ constexpr bool is_mn(int l) { return l == kMN || l == kMNStep; }
 template <typename T, int L> struct Side;
+
+// Buffer descriptor of an MN-contiguous operand's current stage (kElt-byte
+// elements), the record count stopping at the operand's last byte.  Step =
+// false recomputes it from the stage index at each copy; Step = true follows
+// it with two adds per stage.  (Which is faster depends on the kernel:
+// following measured 3% faster where both operands are MN-contiguous, 2%
+// slower for dH.)
+template <bool Step, int kElt>
+struct MNDesc {
+  static constexpr int kStageRows = kStageRowBytes / kElt;  // k-rows per stage
+  int64_t row_bytes;
+  const char* base;  // element (mn0, first k-row of the current stage; of stage 0 if !Step)
+  int64_t bytes;     // bytes from base to the operand's last byte
+  __device__ __forceinline__ void retarget(const void* p, int64_t b) {
+    base = reinterpret_cast<const char*>(p);
+    bytes = b;
+  }
+  __device__ __forceinline__ void step() {
+    if constexpr (Step) {
+      base += kStageRows * row_bytes;
+      bytes -= kStageRows * row_bytes;
+    }
+  }
+  __device__ __forceinline__ u32x4_t rsrc(int64_t kt) const {
+    if constexpr (Step) {
+      return make_rsrc(base, bytes);
+    } else {
+      const int64_t k0 = kt * kStageRows * row_bytes;
+      return make_rsrc(base + k0, bytes - k0);
+    }
+  }
+};
 
 // K-contiguous operand.  A stage is 16 blocks of 1 KiB, each 16 row slots of
 // 64 bytes (four 16-byte chunks, chunk index XOR-swizzled by swz_k(slot)).
@@ -175,6 +209,7 @@ struct SideK {
   __device__ __forceinline__ void retarget(const Operand<T>& op, int64_t mn0) {
     rsrc = make_rsrc(op.base + mn0 * op.ld, (op.mn_ext - mn0) * op.ld * (int64_t)sizeof(T));
   }
+  __device__ __forceinline__ void step() {}  // stages differ by the scalar offset only
   // Per-lane copy and fragment offsets (the same for every tile).
   __device__ __forceinline__ void init_lanes(const Operand<T>& op, int wave, int lane, int sub0) {
     const int64_t row_bytes = op.ld * (int64_t)sizeof(T);
@@ -237,19 +272,16 @@ template <typename T> struct Side<T, kKSplit> : SideK<T, true> {};
 // MN-contiguous bf16 operand: a stage is kStageRowBytes / 2 k-rows x 256 mn.
 // Copy i of wave w covers k-rows 2 (c w + i) and +1 (c = kCopiesPerWave); lane
 // l fills physical chunk l % 32 of k-row 2 (c w + i) + l / 32.
-template <>
-struct Side<__bf16, kMN> {
-  const char* base;       // element (mn0, k = 0)
-  int64_t row_bytes;
-  int64_t k_ext;
-  int64_t mn0_bytes;
+template <bool Step>
+struct SideMNb16 {
+  MNDesc<Step, 2> d;
   uint32_t voff[kCopiesPerWave];
   uint32_t frag_off[kMI];  // per mi: byte offset of this lane's first transposed read
 
   __device__ __forceinline__ void retarget(const Operand<__bf16>& op, int64_t mn0) {
-    base = reinterpret_cast<const char*>(op.base + mn0);
-    mn0_bytes = mn0 * 2;
+    d.retarget(op.base + mn0, op.k_ext * op.ld * 2 - mn0 * 2);
   }
+  __device__ __forceinline__ void step() { d.step(); }
   __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane,
                                        int sub0) {
     init_lanes(op, wave, lane, sub0);
@@ -257,8 +289,8 @@ struct Side<__bf16, kMN> {
   }
   __device__ __forceinline__ void init_lanes(const Operand<__bf16>& op, int wave, int lane,
                                              int sub0) {
-    row_bytes = op.ld * 2;
-    k_ext = op.k_ext;
+    const int64_t row_bytes = op.ld * 2;
+    d.row_bytes = row_bytes;
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) {
       const int kr = 2 * (kCopiesPerWave * wave + i) + (lane >> 5);
@@ -283,10 +315,7 @@ struct Side<__bf16, kMN> {
   }
   __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
                                           int i) const {
-    const int64_t k0 = live ? kt * (kStageRowBytes / 2) : 0;
-    // base points at column mn0: the record count stops at the operand's last byte
-    const u32x4_t r = make_rsrc(base + k0 * row_bytes, (k_ext - k0) * row_bytes - mn0_bytes);
-    dma16(r, dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
+    dma16(d.rsrc(kt), dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
   }
   __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
 #pragma unroll
@@ -305,19 +334,16 @@ struct Side<__bf16, kMN> {
 // MN-contiguous f32 operand: a stage is kStageRowBytes / 4 k-rows of 256
 // floats (1 KiB), one k-row per copy, no swizzle; fragments are read one float
 // at a time.
-template <>
-struct Side<float, kMN> {
-  const char* base;
-  int64_t row_bytes;
-  int64_t k_ext;
-  int64_t mn0_bytes;
+template <bool Step>
+struct SideMNf32 {
+  MNDesc<Step, 4> d;
   uint32_t voff[kCopiesPerWave];
   uint32_t frag_off;
 
   __device__ __forceinline__ void retarget(const Operand<float>& op, int64_t mn0) {
-    base = reinterpret_cast<const char*>(op.base + mn0);
-    mn0_bytes = mn0 * 4;
+    d.retarget(op.base + mn0, op.k_ext * op.ld * 4 - mn0 * 4);
   }
+  __device__ __forceinline__ void step() { d.step(); }
   __device__ __forceinline__ void init(const Operand<float>& op, int64_t mn0, int wave, int lane,
                                        int sub0) {
     init_lanes(op, wave, lane, sub0);
@@ -325,8 +351,8 @@ struct Side<float, kMN> {
   }
   __device__ __forceinline__ void init_lanes(const Operand<float>& op, int wave, int lane,
                                              int sub0) {
-    row_bytes = op.ld * 4;
-    k_ext = op.k_ext;
+    const int64_t row_bytes = op.ld * 4;
+    d.row_bytes = row_bytes;
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) {
       const int kr = kCopiesPerWave * wave + i;
@@ -337,9 +363,7 @@ struct Side<float, kMN> {
   }
   __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
                                           int i) const {
-    const int64_t k0 = live ? kt * (kStageRowBytes / 4) : 0;
-    const u32x4_t r = make_rsrc(base + k0 * row_bytes, (k_ext - k0) * row_bytes - mn0_bytes);
-    dma16(r, dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
+    dma16(d.rsrc(kt), dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
   }
   __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
 #pragma unroll
@@ -354,6 +378,11 @@ struct Side<float, kMN> {
     return v;
   }
 };
+
+template <> struct Side<__bf16, kMN> : SideMNb16<false> {};
+template <> struct Side<__bf16, kMNStep> : SideMNb16<true> {};
+template <> struct Side<float, kMN> : SideMNf32<false> {};
+template <> struct Side<float, kMNStep> : SideMNf32<true> {};
 
 // ---------------------------------------------------------------------------
 // MFMA on one 16-byte fragment pair.
@@ -498,6 +527,8 @@ struct Cursor {
       kt = 0;
       ++ti;
       side.retarget(op, next_mn0);
+    } else {
+      side.step();
     }
   }
 };
@@ -509,8 +540,8 @@ struct Cursor {
 //   H = 1: a[0 .. kMI / 2) and each b[ni], right after its last use, of the
 //          next stage (src = next stage);
 // and, with Copy, the kCopiesPerWave copies of one operand's current stage,
-// one after MFMAs 0 and 4 (measured against other placements: after 1 and
-// 9 dH was 3% and dW 3% slower, the strip kernels the same).  Spreading the
+// one after MFMAs 0 and 4, or 0 and 8 where both operands are MN-contiguous
+// (each measured fastest for its kernels among the placements tried).  Spreading the
 // copies keeps the MFMA pipe fed while the texture unit works through them;
 // issued in a burst, they would hold every wave of the CU at once.
 template <int H, bool Reads, bool Copy, typename T, int AK, int BK, typename C>
@@ -533,12 +564,16 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
       }
     }
     if constexpr (Copy) {
-      if ((t & 3) == 0 && t < 8) cur.copy_one(lds0, off, wave, tiles, t >> 2);
+      if constexpr (is_mn(AK) && is_mn(BK)) {
+        if ((t & 7) == 0) cur.copy_one(lds0, off, wave, tiles, t >> 3);
+      } else {
+        if ((t & 3) == 0 && t < 8) cur.copy_one(lds0, off, wave, tiles, t >> 2);
+      }
     }
     // The order above is pinned where an operand is read with transposing
     // reads (measured faster); with both operands K-contiguous the compiler's
     // own interleaving, with two waves per SIMD, measured faster still.
-    if constexpr (AK == kMN || BK == kMN) sched_fence();
+    if constexpr (is_mn(AK) || is_mn(BK)) sched_fence();
   }
 }
 
@@ -599,8 +634,9 @@ __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>&
 
   // K-contiguous operands take the split placement when both are (strip
   // kernels), the row-major one beside a transposed operand.
-  constexpr int LA = !AK ? kMN : (BK ? kKSplit : kKRow);
-  constexpr int LB = !BK ? kMN : (AK ? kKSplit : kKRow);
+  // MN-contiguous descriptors follow by adds where both operands are (dW).
+  constexpr int LA = !AK ? (BK ? kMN : kMNStep) : (BK ? kKSplit : kKRow);
+  constexpr int LB = !BK ? (AK ? kMN : kMNStep) : (AK ? kKSplit : kKRow);
   Cursor<T, LA> ca{{}, 0, 0, 0u};
   Cursor<T, LB> cb{{}, 0, 0, 0u};
   ca.side.init(A, m0, wave, lane, wm * kWaveM);
