@@ -138,10 +138,22 @@ lce_status_t lce_backward_begin(const lce_problem_t* p, const int32_t* targets,
                                 const float* grad_out, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* Bits of the `accumulate` argument of the backward folds. */
+typedef enum lce_accumulate {
+  LCE_ACC_NONE = 0,
+  LCE_ACC_DHIDDEN = 1, /* d_hidden += G . W_strip instead of = */
+  LCE_ACC_DWEIGHT = 2  /* d_weight_strip += G^T . h instead of = */
+} lce_accumulate_t;
+
 /* Recompute the strip, form its logit gradient G in the workspace, then
- * d_hidden = G . W_strip (accumulate == 0) or d_hidden += G . W_strip
- * (accumulate != 0), and d_weight_strip[v_len, H] = G^T . h (overwritten).
- * The first fold of a backward pass must pass accumulate = 0. */
+ * d_hidden (+)= G . W_strip and d_weight_strip[v_len, H] (+)= G^T . h, each
+ * added to the buffer's contents where its bit of `accumulate` is set
+ * (lce_accumulate_t) and overwriting them otherwise; any other bit is
+ * LCE_ERR_INVALID_VALUE.  The first fold of a backward pass clears
+ * LCE_ACC_DHIDDEN.  LCE_ACC_DWEIGHT serves the second page's Ring-DTP
+ * (section 3.2, appendix C), where one vocabulary shard meets the distinct
+ * batches of several ranks: its weight gradient is the sum of the gradients
+ * of those meetings, and each meeting after the first adds to it. */
 lce_status_t lce_backward_fold(const lce_problem_t* p, const void* hidden,
                                const void* weight_strip, int64_t v_begin, int64_t v_len,
                                const int32_t* targets, const float* lse, float* d_hidden,

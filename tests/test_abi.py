@@ -120,5 +120,9 @@ def test_errors_are_returned_before_any_launch(lib):
     assert lib.lce_forward_fold(ctypes.byref(p), fake, fake, 0, 257, fake, fake, need, None) == 1
     assert lib.lce_backward_fold(ctypes.byref(p), fake, fake, 0, 10, fake, None, fake, 0, fake,
                                  fake, need, None) == 1
+    # accumulate is a bit set of LCE_ACC_DHIDDEN (1) and LCE_ACC_DWEIGHT (2); any other bit fails
+    for bad_bits in (4, 5, -1):
+        assert lib.lce_backward_fold(ctypes.byref(p), fake, fake, 0, 10, fake, fake, fake,
+                                     bad_bits, fake, fake, need, None) == 1
     assert lib.lce_backward(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, need,
                             None) == 1

@@ -150,11 +150,16 @@ def lce_backward_begin(p, targets, grad_out, workspace, stream=None):
                                      _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def _acc_bits(accumulate, accumulate_dw):
+    return (LCE_ACC_DHIDDEN if accumulate else 0) | (LCE_ACC_DWEIGHT if accumulate_dw else 0)
+
+
 def lce_backward_fold(p, hidden, weight_strip, v_begin, v_len, targets, lse, d_hidden,
-                      accumulate, d_weight_strip, workspace, stream=None):
+                      accumulate, d_weight_strip, workspace, stream=None, accumulate_dw=False):
+    """accumulate: add to d_hidden; accumulate_dw: add to d_weight_strip."""
     _check(load().lce_backward_fold(ctypes.byref(p), _ptr(hidden), _ptr(weight_strip), v_begin,
                                     v_len, _ptr(targets), _ptr(lse), _ptr(d_hidden),
-                                    int(bool(accumulate)), _ptr(d_weight_strip),
+                                    _acc_bits(accumulate, accumulate_dw), _ptr(d_weight_strip),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
@@ -166,14 +171,16 @@ def lce_forward_fold_steps(p, hidden, weight_strip, v_begin, v_len, targets, wor
 
 
 def lce_backward_fold_steps(p, hidden, weight_strip, v_begin, v_len, targets, lse, d_hidden,
-                            accumulate, d_weight_strip, workspace, steps, stream=None):
+                            accumulate, d_weight_strip, workspace, steps, stream=None,
+                            accumulate_dw=False):
     _check(load().lce_backward_fold_steps(ctypes.byref(p), _ptr(hidden), _ptr(weight_strip),
                                           v_begin, v_len, _ptr(targets), _ptr(lse),
-                                          _ptr(d_hidden), int(bool(accumulate)),
+                                          _ptr(d_hidden), _acc_bits(accumulate, accumulate_dw),
                                           _ptr(d_weight_strip), _ptr(workspace),
                                           workspace.numel(), steps, _stream(stream)))
 
 
+LCE_ACC_NONE, LCE_ACC_DHIDDEN, LCE_ACC_DWEIGHT = 0, 1, 2
 LCE_STEP_STRIP, LCE_STEP_MERGE = 1, 2
 LCE_STEP_GRAD, LCE_STEP_DHIDDEN, LCE_STEP_DWEIGHT, LCE_STEP_ALL = 1, 2, 4, 7
 

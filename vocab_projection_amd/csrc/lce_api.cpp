@@ -185,18 +185,20 @@ lce_status_t fold_bwd(const Plan& pl, const void* hidden, const void* weight_str
   if (steps & LCE_STEP_GRAD) {
     if ((s = launched(lce::launch_strip_grad<T>(a, st))) != LCE_OK) return s;
   }
+  const int acc_dh = (accumulate & LCE_ACC_DHIDDEN) != 0;
+  const int acc_dw = (accumulate & LCE_ACC_DWEIGHT) != 0;
   if ((steps & LCE_STEP_DHIDDEN) && (steps & LCE_STEP_DWEIGHT)) {
     return launched(lce::launch_dh_dw<T>(a.g_strip, pl.ldg, a.weight_strip, a.hidden, v_len, pl.N,
-                                         pl.H, d_hidden, accumulate, d_weight_strip, st));
+                                         pl.H, d_hidden, acc_dh, d_weight_strip, acc_dw, st));
   }
   if (steps & LCE_STEP_DHIDDEN) {
     s = launched(lce::launch_dh<T>(a.g_strip, pl.ldg, a.weight_strip, v_len, pl.N, pl.H, d_hidden,
-                                   accumulate, st));
+                                   acc_dh, st));
     if (s != LCE_OK) return s;
   }
   if (steps & LCE_STEP_DWEIGHT) {
     s = launched(lce::launch_dw<T>(a.g_strip, pl.ldg, a.hidden, v_len, pl.N, pl.H,
-                                   d_weight_strip, st));
+                                   d_weight_strip, acc_dw, st));
   }
   return s;
 }
@@ -332,6 +334,7 @@ lce_status_t lce_backward_fold_steps(const lce_problem_t* p, const void* hidden,
   if (!aligned(d_hidden) || !aligned(d_weight_strip)) return LCE_ERR_INVALID_VALUE;
   if ((s = check_strip(pl, weight_strip, v_begin, v_len)) != LCE_OK) return s;
   if (steps & ~(unsigned)LCE_STEP_ALL) return LCE_ERR_INVALID_VALUE;
+  if (accumulate & ~(LCE_ACC_DHIDDEN | LCE_ACC_DWEIGHT)) return LCE_ERR_INVALID_VALUE;
   return pl.dtype == LCE_BF16
              ? fold_bwd<__bf16>(pl, hidden, weight_strip, v_begin, v_len, targets, lse, d_hidden,
                                 accumulate, d_weight_strip, ws, steps, stream)
@@ -356,7 +359,8 @@ lce_status_t lce_backward(const lce_problem_t* p, const void* hidden, const void
   for (int64_t v0 = 0; v0 < pl.V; v0 += pl.Vs) {
     const int64_t len = pl.V - v0 < pl.Vs ? pl.V - v0 : pl.Vs;
     s = lce_backward_fold(p, hidden, w + (size_t)v0 * pl.H * pl.elt, v0, len, targets, lse,
-                          d_hidden, v0 != 0, d_weight + (size_t)v0 * pl.H, ws, ws_bytes, stream);
+                          d_hidden, v0 != 0 ? LCE_ACC_DHIDDEN : LCE_ACC_NONE,
+                          d_weight + (size_t)v0 * pl.H, ws, ws_bytes, stream);
     if (s != LCE_OK) return s;
   }
   return LCE_OK;

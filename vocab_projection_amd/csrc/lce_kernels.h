@@ -49,13 +49,13 @@ hipError_t launch_dh(const T* g_strip, int64_t ldg, const T* w_strip, int64_t v_
                      int64_t h, float* d_hidden, int accumulate, hipStream_t st);
 template <typename T>
 hipError_t launch_dw(const T* g_strip, int64_t ldg, const T* hidden, int64_t v_len, int64_t n_tok,
-                     int64_t h, float* d_weight_strip, hipStream_t st);
+                     int64_t h, float* d_weight_strip, int accumulate, hipStream_t st);
 // Both of the above; in one launch that shares the compute units between them
 // when that is shorter than two launches.
 template <typename T>
 hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T* hidden,
-                        int64_t v_len, int64_t n_tok, int64_t h, float* d_hidden, int accumulate,
-                        float* d_weight_strip, hipStream_t st);
+                        int64_t v_len, int64_t n_tok, int64_t h, float* d_hidden, int acc_dh,
+                        float* d_weight_strip, int acc_dw, hipStream_t st);
 
 hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st);
 hipError_t launch_fold(const float2* partials, int64_t n_blocks, float* m, float* s, int64_t n,

@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g)
 // (K-contiguous G, MN-contiguous W_s), the rest dW (MN-contiguous G and h).
 // Both read G and write disjoint outputs, so the compute units can be shared
 // out by work when one of them alone has too few tiles to fill them.
-template <typename T, bool AccumDh>
+template <typename T, bool AccumDh, bool AccumDw>
 __global__ __launch_bounds__(kThreads, 1) void gemm_dh_dw_kernel(GemmArgs<T> dh, GemmArgs<T> dw,
                                                                  int64_t split) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dh_dw_kernel(GemmArgs<T> dh,
     const TileGrid grid{dw.m_tiles, dw.n_tiles, dw.group_m, b - split, gridDim.x - split};
     run_tiles<T, false, false>(A, B, dw.k_len, grid, lds,
                                [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
-                                 gemm_epilogue<T, false>(dw, acc, m0, n0, staging);
+                                 gemm_epilogue<T, AccumDw>(dw, acc, m0, n0, staging);
                                });
   }
 }
@@ -706,9 +706,21 @@ hipError_t launch_dh(const T* g_strip, int64_t ldg, const T* w_strip, int64_t v_
 
 template <typename T>
 hipError_t launch_dw(const T* g_strip, int64_t ldg, const T* hidden, int64_t v_len, int64_t n_tok,
-                     int64_t h, float* d_weight_strip, hipStream_t st) {
-  return launch_gemm<T, false, false, false>(
-      dw_args(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip), st);
+                     int64_t h, float* d_weight_strip, int accumulate, hipStream_t st) {
+  const GemmArgs<T> g = dw_args(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip);
+  return accumulate ? launch_gemm<T, false, false, true>(g, st)
+                    : launch_gemm<T, false, false, false>(g, st);
+}
+
+template <typename T, bool AccumDh, bool AccumDw>
+static hipError_t launch_dh_dw_shared(const GemmArgs<T>& dh, const GemmArgs<T>& dw, int64_t split,
+                                      int64_t blocks, hipStream_t st) {
+  hipError_t e =
+      set_lds<T>(reinterpret_cast<const void*>(&gemm_dh_dw_kernel<T, AccumDh, AccumDw>));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_dh_dw_kernel<T, AccumDh, AccumDw>), dim3((unsigned)blocks),
+                     dim3(kThreads), kLdsBytes, st, dh, dw, split);
+  return hipGetLastError();
 }
 
 // Stages each compute unit runs (the longest block) when `blocks` blocks share
@@ -719,8 +731,8 @@ static int64_t stage_load(int64_t tiles, int64_t nk, int64_t blocks) {
 
 template <typename T>
 hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T* hidden,
-                        int64_t v_len, int64_t n_tok, int64_t h, float* d_hidden, int accumulate,
-                        float* d_weight_strip, hipStream_t st) {
+                        int64_t v_len, int64_t n_tok, int64_t h, float* d_hidden, int acc_dh,
+                        float* d_weight_strip, int acc_dw, hipStream_t st) {
   const GemmArgs<T> dh = dh_args(g_strip, ldg, w_strip, v_len, n_tok, h, d_hidden);
   const GemmArgs<T> dw = dw_args(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip);
   const int64_t t_dh = dh.m_tiles * dh.n_tiles, nk_dh = stages_of<T>(dh.k_len);
@@ -737,21 +749,15 @@ hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T
     }
   }
   if (best_split == 0) {
-    hipError_t e = launch_dh(g_strip, ldg, w_strip, v_len, n_tok, h, d_hidden, accumulate, st);
+    hipError_t e = launch_dh(g_strip, ldg, w_strip, v_len, n_tok, h, d_hidden, acc_dh, st);
     if (e != hipSuccess) return e;
-    return launch_dw(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip, st);
+    return launch_dw(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip, acc_dw, st);
   }
-  const void* fn = accumulate ? reinterpret_cast<const void*>(&gemm_dh_dw_kernel<T, true>)
-                              : reinterpret_cast<const void*>(&gemm_dh_dw_kernel<T, false>);
-  hipError_t e = set_lds<T>(fn);
-  if (e != hipSuccess) return e;
-  if (accumulate)
-    hipLaunchKernelGGL((gemm_dh_dw_kernel<T, true>), dim3((unsigned)p), dim3(kThreads), kLdsBytes,
-                       st, dh, dw, best_split);
-  else
-    hipLaunchKernelGGL((gemm_dh_dw_kernel<T, false>), dim3((unsigned)p), dim3(kThreads),
-                       kLdsBytes, st, dh, dw, best_split);
-  return hipGetLastError();
+  if (acc_dh)
+    return acc_dw ? launch_dh_dw_shared<T, true, true>(dh, dw, best_split, p, st)
+                  : launch_dh_dw_shared<T, true, false>(dh, dw, best_split, p, st);
+  return acc_dw ? launch_dh_dw_shared<T, false, true>(dh, dw, best_split, p, st)
+                : launch_dh_dw_shared<T, false, false>(dh, dw, best_split, p, st);
 }
 
 hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st) {
@@ -790,13 +796,13 @@ template hipError_t launch_dh<__bf16>(const __bf16*, int64_t, const __bf16*, int
 template hipError_t launch_dh<float>(const float*, int64_t, const float*, int64_t, int64_t,
                                      int64_t, float*, int, hipStream_t);
 template hipError_t launch_dw<__bf16>(const __bf16*, int64_t, const __bf16*, int64_t, int64_t,
-                                      int64_t, float*, hipStream_t);
+                                      int64_t, float*, int, hipStream_t);
 template hipError_t launch_dh_dw<__bf16>(const __bf16*, int64_t, const __bf16*, const __bf16*,
-                                         int64_t, int64_t, int64_t, float*, int, float*,
+                                         int64_t, int64_t, int64_t, float*, int, float*, int,
                                          hipStream_t);
 template hipError_t launch_dh_dw<float>(const float*, int64_t, const float*, const float*, int64_t,
-                                        int64_t, int64_t, float*, int, float*, hipStream_t);
+                                        int64_t, int64_t, float*, int, float*, int, hipStream_t);
 template hipError_t launch_dw<float>(const float*, int64_t, const float*, int64_t, int64_t,
-                                     int64_t, float*, hipStream_t);
+                                     int64_t, float*, int, hipStream_t);
 
 }  // namespace lce
