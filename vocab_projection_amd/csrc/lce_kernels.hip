@@ -407,11 +407,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs<T>& g, Acc& acc, in
         old[i] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, off0 + i * step, 0, 0);
     }
     block_barrier();  // staging free: the previous pass (or tile) is done with it
-    if (wm == pass / 2) {
-      // rows 64 (pass % 2) .. +64 of this wave's 128 = sub-tiles mi = 4 (pass % 2) + h
+    constexpr int kPassesPerWave = kWaveM / kEpiRows;
+    if (wm == pass / kPassesPerWave) {
+      // rows kEpiRows (pass % kPassesPerWave) .. + kEpiRows of this wave's kWaveM
 #pragma unroll
       for (int h = 0; h < kEpiRows / kMfma; ++h) {
-        const int mi = (kEpiRows / kMfma) * (pass % 2) + h;
+        const int mi = (kEpiRows / kMfma) * (pass % kPassesPerWave) + h;
 #pragma unroll
         for (int ni = 0; ni < kNI; ++ni) {
           const int col = wn * kWaveN + ni * kMfma + (lane & 15);

@@ -550,7 +550,11 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
                                            uint32_t lds0, uint32_t off, int wave, int64_t tiles,
                                            Acc& acc) {
   constexpr int kHalf = kMI / 2;  // sub-tiles along M per half
-  static_assert(kHalf == 4 && kNI == 4 && kCopiesPerWave == 2, "two copies per half stage");
+  constexpr int kMfmas = kHalf * kNI;
+  // MFMAs between copies: front-loaded (every 4th) unless both operands are
+  // MN-contiguous (spread over the whole half stage)
+  constexpr int kCopyGap = is_mn(AK) && is_mn(BK) ? kMfmas / kCopiesPerWave : 4;
+  static_assert(kHalf == 4 && kCopyGap * kCopiesPerWave <= kMfmas, "copies fit in a half stage");
 #pragma unroll
   for (int t = 0; t < kHalf * kNI; ++t) {
     const int ni = t / kHalf, mi = H * kHalf + t % kHalf;
@@ -564,11 +568,8 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
       }
     }
     if constexpr (Copy) {
-      if constexpr (is_mn(AK) && is_mn(BK)) {
-        if ((t & 7) == 0) cur.copy_one(lds0, off, wave, tiles, t >> 3);
-      } else {
-        if ((t & 3) == 0 && t < 8) cur.copy_one(lds0, off, wave, tiles, t >> 2);
-      }
+      if (t % kCopyGap == 0 && t / kCopyGap < kCopiesPerWave)
+        cur.copy_one(lds0, off, wave, tiles, t / kCopyGap);
     }
     // The order above is pinned where an operand is read with transposing
     // reads (measured faster); with both operands K-contiguous the compiler's
