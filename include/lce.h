@@ -94,9 +94,13 @@ size_t lce_workspace_bytes(const lce_problem_t* p);
 
 /* Forward: loss[0] (float32, device), lse[N] (log-sum-exp of every row,
  * needed by lce_backward) and, if row_loss != NULL, row_loss[N] (0 for
- * ignored rows).  Strips are folded in natural order 0, Vs, 2Vs, ...
- * Equivalent to lce_forward_begin + one lce_forward_fold per strip +
- * lce_forward_end. */
+ * ignored rows).  The vocabulary is folded in natural order.  Equivalent to
+ * lce_forward_begin + lce_forward_fold over consecutive strips +
+ * lce_forward_end, except that one fold here may span several strips: the
+ * forward keeps only 8 bytes of partial state per token and 128 vocabulary
+ * rows, so the workspace holds those of about 32 strips (bf16; 64 for f32)
+ * and each fold takes as many, up to 2^21 rows.  Results agree with the
+ * strip-by-strip calls up to the order of floating-point operations. */
 lce_status_t lce_forward(const lce_problem_t* p, const void* hidden, const void* weight,
                          const int32_t* targets, float* loss, float* lse, float* row_loss,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);

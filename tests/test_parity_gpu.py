@@ -131,6 +131,10 @@ SMALL = [
     # 314 tiles, dH 471; ragged K of 17 stages)
     S.small("bf16_multi_tile", 40123, 520, 1300, 1024, ignore_frac=0.05),
     S.small("f32_multi_tile", 20005, 136, 1100, 1024, "f32", weight_std=0.2, ignore_frac=0.05),
+    # lce_forward folds as many strips per launch as the workspace's partials
+    # hold: here 7936 rows (31 strips of 256), so three folds of 7936, 7936
+    # and 4128 rows
+    S.small("bf16_multi_chunk", 1000, 64, 20000, 256, ignore_frac=0.1),
 ]
 
 
@@ -152,6 +156,18 @@ def test_strip_width_and_fold_order_invariance():
             a, b = o[k].cpu().numpy(), base[k].cpu().numpy()
             assert np.linalg.norm(a - b) <= 1e-3 * np.linalg.norm(b)
     full_check(w, strip=1024, order=S.fold_order(w))
+
+
+def test_wide_forward_folds_match_strip_folds():
+    """lce_forward's multi-strip folds against one lce_forward_fold per strip."""
+    w = S.small("bf16_multi_chunk", 1000, 64, 20000, 256, ignore_frac=0.1)
+    h, W, tt = to_gpu(w, S.hidden(w), S.weight(w), S.targets(w))
+    wide = run_hip(w, h, W, tt)
+    order = [(v0, min(w.strip, w.vocab - v0)) for v0 in range(0, w.vocab, w.strip)]
+    strips = run_hip(w, h, W, tt, order=order)
+    assert abs(wide["loss"] - strips["loss"]) <= 1e-6 * abs(strips["loss"])
+    np.testing.assert_allclose(wide["lse"], strips["lse"], rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(wide["row_loss"], strips["row_loss"], rtol=1e-5, atol=1e-5)
 
 
 def test_deterministic():

@@ -26,6 +26,7 @@ struct Plan {
   int32_t ignore_index;
   size_t elt;
   size_t off_m, off_s, off_zt, off_strip, total;
+  int64_t fwd_chunk;  // widest vocabulary range one forward fold can take (>= Vs)
 };
 
 bool problem_ok(const lce_problem_t* p) {
@@ -48,10 +49,13 @@ size_t elt_of(int dtype) { return dtype == LCE_BF16 ? 2 : 4; }
 
 // Workspace: a 256-byte control block, then one strip region of N x ldg
 // elements.  The backward keeps its gradient strip G there; the forward keeps
-// its per-block partials [ldg / 128, N] of (max, sum) there, followed by the
-// running per-token state (max, sum, target logit), each column padded to 256
-// bytes.  The region is the larger of the two needs; the forward's is smaller
-// except for a handful of tokens.
+// the running per-token state (max, sum, target logit; each column padded to
+// 256 bytes) at the region's end and its per-block partials [blocks, N] of
+// (max, sum) before it.  The region is the larger of the two needs; the
+// forward's is smaller except for a handful of tokens.  A partial takes 8
+// bytes per 128 vocabulary rows, against 128 x elt bytes of G, so the
+// region holds the partials of about 32 (bf16) or 64 (f32) strips beside the
+// state: lce_forward folds that many strips per launch.
 size_t state_col_bytes(int64_t n) { return (size_t)round_up(4 * n, 256); }
 
 size_t partial_bytes(int64_t n, int64_t ldg) { return (size_t)n * (size_t)(ldg / kPartRows) * 8; }
@@ -96,11 +100,16 @@ lce_status_t make_plan(const lce_problem_t* p, Plan* pl) {
   pl->ignore_index = p->ignore_index;
   pl->elt = elt;
   const size_t col = state_col_bytes(pl->N);
-  pl->off_strip = kHeader;
-  pl->off_m = pl->off_strip + partial_bytes(pl->N, pl->ldg);
-  pl->off_s = pl->off_m + col;
-  pl->off_zt = pl->off_s + col;
   pl->total = bytes_for_strip(pl->N, pl->Vs, elt);
+  pl->off_strip = kHeader;
+  pl->off_zt = pl->total - col;
+  pl->off_s = pl->off_zt - col;
+  pl->off_m = pl->off_s - col;
+  // partial blocks that fit before the state; at least ldg / 128 by construction
+  const int64_t blocks = (int64_t)((pl->off_m - pl->off_strip) / ((size_t)pl->N * 8));
+  int64_t chunk = blocks * kPartRows;
+  if (chunk > kMaxStrip) chunk = kMaxStrip;  // same tile-offset bound as one strip
+  pl->fwd_chunk = chunk > pl->Vs ? chunk : pl->Vs;
   return LCE_OK;
 }
 
@@ -288,11 +297,16 @@ lce_status_t lce_forward(const lce_problem_t* p, const void* hidden, const void*
   if (!hidden || !weight || !targets || !loss || !lse) return LCE_ERR_INVALID_VALUE;
   if (!aligned(hidden) || !aligned(weight)) return LCE_ERR_INVALID_VALUE;
   if ((s = lce_forward_begin(p, ws, ws_bytes, stream)) != LCE_OK) return s;
+  // Folds as wide as the workspace's partials allow (several strips each):
+  // fewer, fuller launches; the same kernels as lce_forward_fold.
   const char* w = static_cast<const char*>(weight);
-  for (int64_t v0 = 0; v0 < pl.V; v0 += pl.Vs) {
-    const int64_t len = pl.V - v0 < pl.Vs ? pl.V - v0 : pl.Vs;
-    s = lce_forward_fold(p, hidden, w + (size_t)v0 * pl.H * pl.elt, v0, len, targets, ws,
-                         ws_bytes, stream);
+  const unsigned all = LCE_STEP_STRIP | LCE_STEP_MERGE;
+  for (int64_t v0 = 0; v0 < pl.V; v0 += pl.fwd_chunk) {
+    const int64_t len = pl.V - v0 < pl.fwd_chunk ? pl.V - v0 : pl.fwd_chunk;
+    const void* ws_rows = w + (size_t)v0 * pl.H * pl.elt;
+    s = pl.dtype == LCE_BF16
+            ? fold_fwd<__bf16>(pl, hidden, ws_rows, v0, len, targets, ws, all, stream)
+            : fold_fwd<float>(pl, hidden, ws_rows, v0, len, targets, ws, all, stream);
     if (s != LCE_OK) return s;
   }
   return lce_forward_end(p, targets, loss, lse, row_loss, ws, ws_bytes, stream);

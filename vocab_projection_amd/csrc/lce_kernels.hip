@@ -507,17 +507,47 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float mp, float sp
   m = mn;
 }
 
-__global__ void fold_kernel(const float2* __restrict__ partials, int64_t n_blocks, float* m,
-                            float* s, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float mm = m[i], ss = s[i];
-  for (int64_t b = 0; b < n_blocks; ++b) {
-    const float2 p = partials[b * n + i];
-    lse_merge(mm, ss, p.x, p.y);
+// Fold partials [n_blocks, n] into the running state (m, s) [n]: a block of
+// kFoldWays waves takes 64 consecutive tokens (one per lane, so every load is
+// 512 contiguous bytes); wave w merges the partial blocks w, w + kFoldWays,
+// ... of its tokens, then wave 0 merges the kFoldWays results in wave order
+// and the state.  The order of merges is fixed, so results do not depend on
+// timing.  Spreading the blocks over waves keeps enough loads in flight when
+// there are few tokens and many blocks (a whole vocabulary in one fold).
+constexpr int kFoldWays = 16;
+
+__global__ __launch_bounds__(64 * kFoldWays) void fold_kernel(const float2* __restrict__ partials,
+                                                              int64_t n_blocks, float* m, float* s,
+                                                              int64_t n) {
+  __shared__ float2 part[kFoldWays][64];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
+  float mm = -INFINITY, ss = 0.f;
+  if (i < n) {
+    int64_t b = w;
+    for (; b + 3 * kFoldWays < n_blocks; b += 4 * kFoldWays) {
+      float2 p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) p[u] = partials[(b + u * kFoldWays) * n + i];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lse_merge(mm, ss, p[u].x, p[u].y);
+    }
+    for (; b < n_blocks; b += kFoldWays) {
+      const float2 p = partials[b * n + i];
+      lse_merge(mm, ss, p.x, p.y);
+    }
   }
-  m[i] = mm;
-  s[i] = ss;
+  part[w][lane] = float2{mm, ss};
+  __syncthreads();
+  if (w == 0 && i < n) {
+    mm = m[i];
+    ss = s[i];
+#pragma unroll
+    for (int k = 0; k < kFoldWays; ++k) lse_merge(mm, ss, part[k][lane].x, part[k][lane].y);
+    m[i] = mm;
+    s[i] = ss;
+  }
 }
 
 constexpr int kReduceThreads = 1024;
@@ -622,6 +652,9 @@ static int64_t grid_blocks(int64_t tiles, int64_t nk) {
   return tiles < p ? tiles : p;
 }
 
+// A grid of one block per tile can only be launched up to 2^31 - 1 blocks.
+static bool grid_ok(int64_t blocks) { return blocks >= 1 && blocks <= 0x7fffffffLL; }
+
 template <typename T>
 static int64_t stages_of(int64_t k_len) {
   constexpr int64_t kStageK = kStageRowBytes / sizeof(T);
@@ -634,6 +667,7 @@ hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st) {
   a.n_tiles = cdiv(a.N, kTile);
   a.group_m = kStripGroupM;
   const int64_t blocks = grid_blocks(a.m_tiles * a.n_tiles, stages_of<T>(a.H));
+  if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_lse_kernel<T>));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(strip_lse_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, st, a);
@@ -646,6 +680,7 @@ hipError_t launch_strip_grad(StripArgs<T> a, hipStream_t st) {
   a.n_tiles = cdiv(a.N, kTile);
   a.group_m = kStripGroupM;
   const int64_t blocks = grid_blocks(a.m_tiles * a.n_tiles, stages_of<T>(a.H));
+  if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_grad_kernel<T>));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(strip_grad_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, st, a);
@@ -658,6 +693,7 @@ static hipError_t launch_gemm(GemmArgs<T> g, hipStream_t st) {
   g.n_tiles = cdiv(g.n, kTile);
   g.group_m = kGemmGroupM;
   const int64_t blocks = grid_blocks(g.m_tiles * g.n_tiles, stages_of<T>(g.k_len));
+  if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
   hipError_t e =
       set_lds<T>(reinterpret_cast<const void*>(&gemm_f32out_kernel<T, AK, BK, Accum>));
   if (e != hipSuccess) return e;
@@ -768,8 +804,8 @@ hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream
 
 hipError_t launch_fold(const float2* partials, int64_t n_blocks, float* m, float* s, int64_t n,
                        hipStream_t st) {
-  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, partials,
-                     n_blocks, m, s, n);
+  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)cdiv(n, 64)), dim3(64 * kFoldWays), 0, st,
+                     partials, n_blocks, m, s, n);
   return hipGetLastError();
 }
 
