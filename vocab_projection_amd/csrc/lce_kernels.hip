@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads, 1) void strip_lse_kernel(StripArgs<T> a) 
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<T> B{a.hidden, a.H, a.N, a.H};
-  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x};
+  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
   run_tiles<T, true, true>(A, B, a.H, grid, lds,
                            [&](Acc& acc, int64_t m0, int64_t n0, char*) {
                              lse_epilogue(a, acc, m0, n0);
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const Operand<T> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<T> B{a.hidden, a.H, a.N, a.H};
-  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x};
+  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
   run_tiles<T, true, true>(A, B, a.H, grid, lds,
                            [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
                              grad_epilogue(a, acc, m0, n0, staging);
@@ -367,6 +367,10 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
 // per instruction.  With Accum a pass issues half of its loads of C before
 // the staging writes, so that their latency hides behind them.
 // ---------------------------------------------------------------------------
+// Tile order of the fp32-output GEMMs: bands of groups (see TileGrid) or one
+// contiguous range of the group order per XCD.
+constexpr bool kGemmBands = false;
+
 constexpr int kEpiRows = 64;                        // rows of C per pass
 constexpr int kEpiRowBytes = kTile * 4;             // one row of C in LDS
 static_assert(kEpiRows * kEpiRowBytes <= kStagingBytes, "epilogue staging fits in LDS");
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g)
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const Operand<T> A{g.a, g.lda, g.a_mn_ext, g.a_k_ext};
   const Operand<T> B{g.b, g.ldb, g.b_mn_ext, g.b_k_ext};
-  const TileGrid grid{g.m_tiles, g.n_tiles, g.group_m, blockIdx.x, gridDim.x};
+  const TileGrid grid{g.m_tiles, g.n_tiles, g.group_m, blockIdx.x, gridDim.x, kGemmBands};
   run_tiles<T, AK, BK>(A, B, g.k_len, grid, lds,
                        [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
                          gemm_epilogue<T, Accum>(g, acc, m0, n0, staging);
@@ -471,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dh_dw_kernel(GemmArgs<T> dh,
   if (b < split) {
     const Operand<T> A{dh.a, dh.lda, dh.a_mn_ext, dh.a_k_ext};
     const Operand<T> B{dh.b, dh.ldb, dh.b_mn_ext, dh.b_k_ext};
-    const TileGrid grid{dh.m_tiles, dh.n_tiles, dh.group_m, b, split};
+    const TileGrid grid{dh.m_tiles, dh.n_tiles, dh.group_m, b, split, kGemmBands};
     run_tiles<T, true, false>(A, B, dh.k_len, grid, lds,
                               [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
                                 gemm_epilogue<T, AccumDh>(dh, acc, m0, n0, staging);
@@ -479,7 +483,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dh_dw_kernel(GemmArgs<T> dh,
   } else {
     const Operand<T> A{dw.a, dw.lda, dw.a_mn_ext, dw.a_k_ext};
     const Operand<T> B{dw.b, dw.ldb, dw.b_mn_ext, dw.b_k_ext};
-    const TileGrid grid{dw.m_tiles, dw.n_tiles, dw.group_m, b - split, gridDim.x - split};
+    const TileGrid grid{dw.m_tiles, dw.n_tiles, dw.group_m, b - split, gridDim.x - split,
+                        kGemmBands};
     run_tiles<T, false, false>(A, B, dw.k_len, grid, lds,
                                [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
                                  gemm_epilogue<T, AccumDw>(dw, acc, m0, n0, staging);

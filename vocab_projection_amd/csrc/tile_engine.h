@@ -471,35 +471,56 @@ constexpr int kXcds = 8;  // blocks are dispatched to the 8 XCDs round-robin
 
 // Tiles of an M x N output, ordered in groups of group_m M-tiles: within a
 // group N advances after every group_m tiles, so that consecutive tiles share
-// operand rows.  Each XCD (block b runs on XCD b % 8) is given one contiguous
-// range of that order, so the tiles resident on one XCD at the same time are
-// neighbours and share its L2.  Block `block` of the `blocks` that work on
-// this output takes the tiles of virtual blocks block, block + G, block + 2G,
-// ... (G = blocks; G is the tile count or a multiple of 8, and the first block
-// of the output sits at a multiple of 8 in the grid, so that every virtual
-// block maps to the XCD of its block).
+// operand rows.  Groups are dealt out in bands of kXcds groups, one group of a
+// band to each XCD (block b runs on XCD b % 8): the XCDs then walk N in step,
+// so an operand panel along N that one XCD reads is read by the others at
+// about the same time and comes from the shared MALL rather than HBM again.
+// (Without bands, an output many groups tall puts each XCD on its own stretch
+// of N.)  The M-tiles past the last full band form one partial band, whose
+// group order is split into kXcds contiguous ranges, one per XCD.  Either way
+// the tiles resident on one XCD at the same time are neighbours and share its
+// L2.  Block `block` of the `blocks` that work on this output takes the tiles
+// of virtual blocks block, block + G, block + 2G, ... (G = blocks; G is the
+// tile count or a multiple of 8, and the first block of the output sits at a
+// multiple of 8 in the grid, so that every virtual block maps to the XCD of
+// its block).  Virtual block v is the (v / 8)-th tile of XCD v % 8; each XCD
+// has total / 8 tiles, one more for the first total % 8, which is exactly its
+// share of [0, total), so the order is a bijection.
 struct TileGrid {
   int64_t m_tiles, n_tiles, group_m;
   int64_t block, blocks;
+  bool bands;  // deal groups out in bands; false: the whole order is one partial band
 
-  __device__ __forceinline__ int64_t total() const { return m_tiles * n_tiles; }
+  __host__ __device__ __forceinline__ int64_t total() const { return m_tiles * n_tiles; }
   // Tiles taken by this block (zero if it is past the last tile).
-  __device__ __forceinline__ int64_t count() const {
+  __host__ __device__ __forceinline__ int64_t count() const {
     return (total() - block + blocks - 1) / blocks;
   }
   // First row and column of this block's i-th tile.
-  __device__ __forceinline__ void coords(int64_t i, int64_t* m0, int64_t* n0) const {
+  __host__ __device__ __forceinline__ void coords(int64_t i, int64_t* m0, int64_t* n0) const {
     const int64_t b = block + i * blocks;
     const int64_t x = b % kXcds, j = b / kXcds;
-    const int64_t q = total() / kXcds, r = total() % kXcds;
-    const int64_t t = x * q + (x < r ? x : r) + j;  // a bijection of [0, total)
-    const int64_t per_group = group_m * n_tiles;
-    const int64_t g = t / per_group;
-    const int64_t first_m = g * group_m;
-    const int64_t gm = m_tiles - first_m < group_m ? m_tiles - first_m : group_m;
-    const int64_t local = t - g * per_group;
-    *m0 = (first_m + local % gm) * kTile;
-    *n0 = (local / gm) * kTile;
+    const int64_t band_m = kXcds * group_m;
+    const int64_t full = bands ? m_tiles / band_m : 0;  // full bands
+    const int64_t per_xcd = group_m * n_tiles;    // one group: an XCD's share of a band
+    int64_t m, n;
+    if (j < full * per_xcd) {
+      const int64_t band = j / per_xcd, local = j - band * per_xcd;
+      m = band * band_m + x * group_m + local % group_m;
+      n = local / group_m;
+    } else {
+      const int64_t m_base = full * band_m, rem = m_tiles - m_base;
+      const int64_t tot = rem * n_tiles, q = tot / kXcds, r = tot % kXcds;
+      const int64_t t = x * q + (x < r ? x : r) + (j - full * per_xcd);
+      const int64_t g = t / per_xcd;
+      const int64_t first_m = g * group_m;
+      const int64_t gm = rem - first_m < group_m ? rem - first_m : group_m;
+      const int64_t local = t - g * per_xcd;
+      m = m_base + first_m + local % gm;
+      n = local / gm;
+    }
+    *m0 = m * kTile;
+    *n0 = n * kTile;
   }
 };
 
