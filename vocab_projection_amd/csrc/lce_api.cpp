@@ -303,10 +303,10 @@ lce_status_t lce_forward(const lce_problem_t* p, const void* hidden, const void*
   const unsigned all = LCE_STEP_STRIP | LCE_STEP_MERGE;
   for (int64_t v0 = 0; v0 < pl.V; v0 += pl.fwd_chunk) {
     const int64_t len = pl.V - v0 < pl.fwd_chunk ? pl.V - v0 : pl.fwd_chunk;
-    const void* ws_rows = w + (size_t)v0 * pl.H * pl.elt;
+    const void* w_rows = w + (size_t)v0 * pl.H * pl.elt;
     s = pl.dtype == LCE_BF16
-            ? fold_fwd<__bf16>(pl, hidden, ws_rows, v0, len, targets, ws, all, stream)
-            : fold_fwd<float>(pl, hidden, ws_rows, v0, len, targets, ws, all, stream);
+            ? fold_fwd<__bf16>(pl, hidden, w_rows, v0, len, targets, ws, all, stream)
+            : fold_fwd<float>(pl, hidden, w_rows, v0, len, targets, ws, all, stream);
     if (s != LCE_OK) return s;
   }
   return lce_forward_end(p, targets, loss, lse, row_loss, ws, ws_bytes, stream);
