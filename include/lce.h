@@ -136,6 +136,33 @@ lce_status_t lce_forward_end(const lce_problem_t* p, const int32_t* targets, flo
                              float* lse, float* row_loss, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Merging running states: a vocabulary split across devices ----
+ * When every device holds the whole token batch and one vocabulary shard
+ * (the vocabulary-parallel reduction that the second page's section 5
+ * contrasts with Ring-DTP, and the vocab_partition of the first page's
+ * full-logits formula), each device folds its shard into its own running
+ * state, and the states are combined token by token: (max, sum of
+ * exponentials) by the associative log-sum-exp merge, the target logit from
+ * the shard that holds the target.  These two calls export a state and fold
+ * an exported one into a workspace, so that states can be exchanged between
+ * devices (an all-gather, a ring) and merged before lce_forward_end.  The
+ * backward pass then needs no exchange but the sum of the devices'
+ * d_hidden: each device runs lce_backward_begin and lce_backward_fold over
+ * its own shard with the merged lse. */
+
+/* Copy the workspace's running state to state[3 * N] (float32): row 0 the
+ * per-token max, row 1 the sum of exp(z - max), row 2 the target logit (NaN
+ * while the target has not been folded). */
+lce_status_t lce_forward_state(const lce_problem_t* p, float* state, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Fold a state written by lce_forward_state, for the same tokens and a part of
+ * the vocabulary disjoint from the one already folded here, into the
+ * workspace's running state (a target logit is taken from whichever side has
+ * one; with both, this side's is kept). */
+lce_status_t lce_forward_merge_state(const lce_problem_t* p, const float* state, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
 /* Count the non-ignored rows and form the per-row gradient scale from the
  * device scalar grad_out (grad_out / n_valid for mean, grad_out for sum). */
 lce_status_t lce_backward_begin(const lce_problem_t* p, const int32_t* targets,

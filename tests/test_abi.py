@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(names) == sorted(B.EXPORTS)
@@ -120,6 +120,10 @@ def test_errors_are_returned_before_any_launch(lib):
     assert lib.lce_forward_fold(ctypes.byref(p), fake, fake, 0, 257, fake, fake, need, None) == 1
     assert lib.lce_backward_fold(ctypes.byref(p), fake, fake, 0, 10, fake, None, fake, 0, fake,
                                  fake, need, None) == 1
+    assert lib.lce_forward_state(ctypes.byref(p), None, fake, need, None) == 1
+    assert lib.lce_forward_merge_state(ctypes.byref(p), None, fake, need, None) == 1
+    assert lib.lce_forward_state(ctypes.byref(p), fake, fake, need - 1, None) == 3
+    assert lib.lce_forward_merge_state(ctypes.byref(P(n=0)), fake, fake, need, None) == 1
     # accumulate is a bit set of LCE_ACC_DHIDDEN (1) and LCE_ACC_DWEIGHT (2); any other bit fails
     for bad_bits in (4, 5, -1):
         assert lib.lce_backward_fold(ctypes.byref(p), fake, fake, 0, 10, fake, fake, fake,

@@ -48,6 +48,8 @@ _SIGNATURES = {
     "lce_forward_begin": (ctypes.c_int, [_P, _VP, _SZ, _VP]),
     "lce_forward_fold": (ctypes.c_int, [_P, _VP, _VP, _I64, _I64, _VP, _VP, _SZ, _VP]),
     "lce_forward_end": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "lce_forward_state": (ctypes.c_int, [_P, _VP, _VP, _SZ, _VP]),
+    "lce_forward_merge_state": (ctypes.c_int, [_P, _VP, _VP, _SZ, _VP]),
     "lce_backward_begin": (ctypes.c_int, [_P, _VP, _VP, _VP, _SZ, _VP]),
     "lce_backward_fold": (ctypes.c_int, [_P, _VP, _VP, _I64, _I64, _VP, _VP, _VP, ctypes.c_int,
                                          _VP, _VP, _SZ, _VP]),
@@ -143,6 +145,18 @@ def lce_forward_end(p, targets, loss, lse, row_loss, workspace, stream=None):
     _check(load().lce_forward_end(ctypes.byref(p), _ptr(targets), _ptr(loss), _ptr(lse),
                                   _ptr(row_loss), _ptr(workspace), workspace.numel(),
                                   _stream(stream)))
+
+
+def lce_forward_state(p, state, workspace, stream=None):
+    """Copy the running state into state (float32, 3 * N: max, sum, target logit)."""
+    _check(load().lce_forward_state(ctypes.byref(p), _ptr(state), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
+
+
+def lce_forward_merge_state(p, state, workspace, stream=None):
+    """Fold a state exported by lce_forward_state (a disjoint vocabulary part) into workspace."""
+    _check(load().lce_forward_merge_state(ctypes.byref(p), _ptr(state), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)))
 
 
 def lce_backward_begin(p, targets, grad_out, workspace, stream=None):

@@ -312,6 +312,28 @@ lce_status_t lce_forward(const lce_problem_t* p, const void* hidden, const void*
   return lce_forward_end(p, targets, loss, lse, row_loss, ws, ws_bytes, stream);
 }
 
+lce_status_t lce_forward_state(const lce_problem_t* p, float* state, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
+  if (!state) return LCE_ERR_INVALID_VALUE;
+  Carve c = carve(pl, ws);
+  return launched(lce::launch_state_export(c.m, c.s, c.zt, state, pl.N, stream));
+}
+
+lce_status_t lce_forward_merge_state(const lce_problem_t* p, const float* state, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
+  if (!state) return LCE_ERR_INVALID_VALUE;
+  Carve c = carve(pl, ws);
+  return launched(lce::launch_state_merge(state, c.m, c.s, c.zt, pl.N, stream));
+}
+
 lce_status_t lce_backward_begin(const lce_problem_t* p, const int32_t* targets,
                                 const float* grad_out, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {

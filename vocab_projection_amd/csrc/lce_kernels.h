@@ -60,6 +60,10 @@ hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T
 hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st);
 hipError_t launch_fold(const float2* partials, int64_t n_blocks, float* m, float* s, int64_t n,
                        hipStream_t st);
+hipError_t launch_state_export(const float* m, const float* s, const float* zt, float* state,
+                               int64_t n, hipStream_t st);
+hipError_t launch_state_merge(const float* state, float* m, float* s, float* zt, int64_t n,
+                              hipStream_t st);
 hipError_t launch_finalize(const float* m, const float* s, const float* zt, const int32_t* targets,
                            int64_t n, int32_t ignore_index, int reduction, float* lse,
                            float* row_loss, float* loss, hipStream_t st);

@@ -555,6 +555,31 @@ __global__ __launch_bounds__(64 * kFoldWays) void fold_kernel(const float2* __re
   }
 }
 
+// The running state as three rows [3, n] (max, sum, target logit), out and in.
+__global__ void state_export_kernel(const float* __restrict__ m, const float* __restrict__ s,
+                                    const float* __restrict__ zt, float* __restrict__ state,
+                                    int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    state[i] = m[i];
+    state[n + i] = s[i];
+    state[2 * n + i] = zt[i];
+  }
+}
+
+__global__ void state_merge_kernel(const float* __restrict__ state, float* m, float* s, float* zt,
+                                   int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    float mm = m[i], ss = s[i];
+    lse_merge(mm, ss, state[i], state[n + i]);
+    m[i] = mm;
+    s[i] = ss;
+    const float z = zt[i];
+    if (z != z) zt[i] = state[2 * n + i];  // NaN: the target was not folded on this side
+  }
+}
+
 constexpr int kReduceThreads = 1024;
 
 // One block: lse, row loss, n_valid and the reduced loss (fixed-order sums).
@@ -811,6 +836,20 @@ hipError_t launch_fold(const float2* partials, int64_t n_blocks, float* m, float
                        hipStream_t st) {
   hipLaunchKernelGGL(fold_kernel, dim3((unsigned)cdiv(n, 64)), dim3(64 * kFoldWays), 0, st,
                      partials, n_blocks, m, s, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_export(const float* m, const float* s, const float* zt, float* state,
+                               int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(state_export_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, m, s, zt,
+                     state, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_merge(const float* state, float* m, float* s, float* zt, int64_t n,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(state_merge_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, state, m,
+                     s, zt, n);
   return hipGetLastError();
 }
 
