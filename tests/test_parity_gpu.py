@@ -158,6 +158,36 @@ def test_strip_width_and_fold_order_invariance():
     full_check(w, strip=1024, order=S.fold_order(w))
 
 
+def test_strip_width_policy():
+    """The strip-width policy end to end: strip = 0 takes the widest strip the
+    default 2 GiB budget allows (here the whole vocabulary), and
+    lce_pick_strip for a 1 MiB budget gives strips of 512; either way the
+    workspace is what lce_workspace_bytes states and the results match the
+    oracle."""
+    w = S.small("bf16_policy", 1000, 128, 5000, 5000, ignore_frac=0.1)
+    hid, wt, t = S.hidden(w), S.weight(w), S.targets(w)
+    h, W, tt = to_gpu(w, hid, wt, t)
+    p0 = B.make_problem(h, W, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, strip=0)
+    assert B.lce_workspace_bytes(p0) == 256 + 1000 * 5120 * 2
+    vs = B.lce_pick_strip(p0, 1 << 20)
+    assert vs == 512
+    p1 = B.make_problem(h, W, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, strip=vs)
+    assert B.lce_workspace_bytes(p1) <= 1 << 20
+    loss_ref, lse_ref, _ = O.forward(hid, wt, t, ignore_index=S.IGNORE_INDEX, reduction=w.reduction)
+    dh_ref, dw_ref = O.backward(hid, wt, t, ignore_index=S.IGNORE_INDEX, reduction=w.reduction)
+    go = torch.ones(1, dtype=torch.float32, device=DEV)
+    for strip in (0, vs):
+        loss, lse = B.forward(h, W, tt, ignore_index=S.IGNORE_INDEX, reduction=w.reduction,
+                              strip=strip)
+        dh, dw = B.backward(h, W, tt, lse, go, ignore_index=S.IGNORE_INDEX,
+                            reduction=w.reduction, strip=strip)
+        torch.cuda.synchronize()
+        assert_loss(w, loss.item(), loss_ref)
+        assert_lse(lse.cpu().numpy(), lse_ref)
+        assert_grad(w, dh.cpu().numpy(), dh_ref, f"dH strip {strip}")
+        assert_grad(w, dw.cpu().numpy(), dw_ref, f"dW strip {strip}")
+
+
 def test_wide_forward_folds_match_strip_folds():
     """lce_forward's multi-strip folds against one lce_forward_fold per strip."""
     w = S.small("bf16_multi_chunk", 1000, 64, 20000, 256, ignore_frac=0.1)
