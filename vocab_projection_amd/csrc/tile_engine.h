@@ -10,8 +10,9 @@
 // are copied from global memory straight into LDS with buffer_load ... lds
 // (no register staging) into a ring of kStages buffers, so a stage is copied
 // kStages - 1 stages before it is read.
-// The copies of a stage are spread over the MFMAs of the stage before: one
-// wave-wide copy after every fourth MFMA.  The texture unit takes many cycles
+// The copies of a stage are spread over the MFMAs of the stage before: two
+// wave-wide copies per half stage of 16 MFMAs, after MFMAs 0 and 4 (0 and 8
+// where both operands are MN-contiguous).  The texture unit takes many cycles
 // per 1 KiB copy and is shared by the CU's waves, so copies issued in a
 // burst stall every wave's MFMA issue at once; spread out, they hide behind
 // the MFMAs.  The lead given by the ring is what lets them be spread.
@@ -30,8 +31,10 @@
 //    index swizzled by the k-row) and read with ds_read_b64_tr_b16, which
 //    hands each lane four K values of one column; two such reads make a
 //    fragment.  f32 stages (16 k-rows of 1 KiB) are read one float at a time.
-// Both bf16 swizzles keep every fragment read free of LDS bank conflicts
-// (64 four-byte banks, 256 bytes per cycle).
+// The MN-contiguous swizzle and the split K-contiguous placement (below) keep
+// every fragment read free of LDS bank conflicts (64 four-byte banks, 256
+// bytes per cycle); the row-major K-contiguous placement, kept beside a
+// transposed operand where it measured faster, costs a 2-way conflict.
 //
 // Loads go through buffer resources whose record count ends at the last
 // valid row, so rows past the operand's extent read as zeros and nothing is
