@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--strip", type=int, default=0,
+                    help="strip width Vs instead of the workload's (natural fold order only)")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,6 +76,12 @@ def main():
     from vocab_projection_amd import synthetic as S
 
     w = S.WORKLOADS[args.workload]
+    if args.strip:
+        if w.shards:
+            print("--strip applies to workloads folded in natural order", file=sys.stderr)
+            sys.exit(2)
+        # another configuration: its own name, so no stored counter summary applies
+        w = w.with_(strip=args.strip, name=f"{w.name}_strip{args.strip}")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
