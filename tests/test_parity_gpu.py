@@ -351,6 +351,15 @@ def test_full_size_sampled(name):
     ref_dw = O.weight_grad_rows(hid, wt[vids], vids, t, g["lse"], sc)
     e2 = assert_grad(w, out["dw"][torch.from_numpy(vids).to(DEV)].cpu().numpy(), ref_dw, "dW rows")
     say(f"{name}: dW rows checked {time.time() - t0:.1f}s err {e2:.2e}")
+    # run-to-run: bit-identical results, the second time from a workspace
+    # filled with NaN bytes (no result may depend on timing or on what the
+    # workspace held before)
+    again = run_hip(w, h, W, tt, order=order, poison=True)
+    assert again["loss"] == out["loss"]
+    assert np.array_equal(again["lse"], out["lse"])
+    assert torch.equal(again["dh"], out["dh"]) and torch.equal(again["dw"], out["dw"])
+    del again
+    say(f"{name}: second run bit-identical {time.time() - t0:.1f}s")
     # invariants at full size
     ign = torch.from_numpy(np.nonzero(t == S.IGNORE_INDEX)[0]).to(DEV)
     if ign.numel():
