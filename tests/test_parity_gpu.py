@@ -158,6 +158,33 @@ def test_strip_width_and_fold_order_invariance():
     full_check(w, strip=1024, order=S.fold_order(w))
 
 
+def test_ignore_index_inside_the_vocabulary():
+    """ignore_index may be a valid vocabulary id: rows with that target are
+    left out (loss, mean denominator and gradients), while the id's logits
+    still count in every other row's log-sum-exp."""
+    w = S.small("bf16_ignore_inside", 700, 96, 2500, 1024, ignore_frac=0.0)
+    hid, wt, t = S.hidden(w), S.weight(w), S.targets(w).copy()
+    t[::9] = 7                      # one row in nine targets id 7, now the ignore index
+    h, W, tt = to_gpu(w, hid, wt, t)
+    p = B.make_problem(h, W, ignore_index=7, reduction="mean", strip=w.strip)
+    ws = B.workspace(p, DEV)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    lse = torch.empty(w.n_tokens, dtype=torch.float32, device=DEV)
+    dh = torch.empty(h.shape, dtype=torch.float32, device=DEV)
+    dw = torch.empty(W.shape, dtype=torch.float32, device=DEV)
+    go = torch.ones(1, dtype=torch.float32, device=DEV)
+    B.lce_forward(p, h, W, tt, loss, lse, None, ws)
+    B.lce_backward(p, h, W, tt, lse, go, dh, dw, ws)
+    torch.cuda.synchronize()
+    ref_loss, ref_lse, _ = O.forward(hid, wt, t, ignore_index=7, reduction="mean")
+    ref_dh, ref_dw = O.backward(hid, wt, t, ignore_index=7, reduction="mean")
+    assert_loss(w, loss.item(), ref_loss)
+    assert_lse(lse.cpu().numpy(), ref_lse)
+    assert_grad(w, dh.cpu().numpy(), ref_dh, "dH")
+    assert_grad(w, dw.cpu().numpy(), ref_dw, "dW")
+    assert torch.count_nonzero(dh[::9]).item() == 0
+
+
 def test_strip_width_policy():
     """The strip-width policy end to end: strip = 0 takes the widest strip the
     default 2 GiB budget allows (here the whole vocabulary), and
