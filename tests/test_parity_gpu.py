@@ -158,6 +158,26 @@ def test_strip_width_and_fold_order_invariance():
     full_check(w, strip=1024, order=S.fold_order(w))
 
 
+def test_vocabulary_of_one():
+    """V = 1 with the smallest bf16 hidden size (H = 8): every logit is its
+    row's lse, every row loss is 0, and G = g (1 - 1) = 0, so both gradients
+    are 0 (the oracle exactly; the kernels up to one fp32 rounding inside
+    exp2, which leaves softmax = 1 within 2^-23)."""
+    w = S.small("bf16_vocab_one", 37, 8, 1, 1, ignore_frac=0.2)
+    hid, wt, t = S.hidden(w), S.weight(w), S.targets(w)
+    assert set(np.unique(t)) <= {0, S.IGNORE_INDEX}
+    h, W, tt = to_gpu(w, hid, wt, t)
+    out = run_hip(w, h, W, tt)
+    ref_loss, ref_lse, _ = O.forward(hid, wt, t, ignore_index=S.IGNORE_INDEX, reduction="mean")
+    z = hid.astype(np.float64) @ wt.astype(np.float64).T
+    assert ref_loss == 0.0 and abs(out["loss"]) <= 1e-6
+    np.testing.assert_allclose(out["lse"], z[:, 0], rtol=1e-6, atol=1e-6)
+    assert_lse(out["lse"], ref_lse)
+    assert np.abs(out["row_loss"]).max() <= 1e-6
+    assert out["dh"].abs().max().item() <= 1e-6
+    assert out["dw"].abs().max().item() <= 1e-6
+
+
 def test_ignore_index_inside_the_vocabulary():
     """ignore_index may be a valid vocabulary id: rows with that target are
     left out (loss, mean denominator and gradients), while the id's logits
