@@ -135,6 +135,12 @@ SMALL = [
     # hold: here 7936 rows (31 strips of 256), so three folds of 7936, 7936
     # and 4128 rows
     S.small("bf16_multi_chunk", 1000, 64, 20000, 256, ignore_frac=0.1),
+    # one token (255 masked rows in its only token tile) against a long
+    # hidden size and a large vocabulary: one forward launch of 274 tiles
+    S.small("bf16_one_token_long_h", 1, 4096, 70000, 8192, weight_std=0.02),
+    # few tokens, a vocabulary past 2^18: the forward's folds of up to
+    # 261888 rows split it in two (261888 + 38112)
+    S.small("bf16_small_n_huge_v", 300, 64, 300000, 8192, ignore_frac=0.1),
 ]
 
 
