@@ -219,17 +219,27 @@ def measured_traffic(workload: str, step: str):
 
 
 def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, loss, peak):
-    """Run the same steps through the step-level calls with an event pair around
-    every kernel launch of the fold loops; return per-kernel times and the
-    roofline of the kernel with the largest total time."""
+    """Run the timed step's launches again, one call per kernel, with an event
+    pair around each on the stream the library launches on; return per-kernel
+    times and the roofline of the kernel with the largest total time.
+
+    The launches are those of the timed step: in natural order the forward
+    folds as lce_forward does (ranges of lce_forward_fold_max rows, so one
+    strip_lse launch over the whole vocabulary when it fits), and each strip of
+    the backward runs strip_grad, then dH and dW as two launches or as the one
+    shared launch that lce_backward_fold makes for that strip."""
     kernels = {
-        "strip_lse": ("lce::strip_lse_kernel", "fwd", B.LCE_STEP_STRIP),
-        "merge": ("lce::fold_kernel", "fwd", B.LCE_STEP_MERGE),
-        "strip_grad": ("lce::strip_grad_kernel", "bwd", B.LCE_STEP_GRAD),
-        "gemm_dh": ("lce::gemm_f32out_kernel<A K-contig, B MN-contig>", "bwd", B.LCE_STEP_DHIDDEN),
-        "gemm_dw": ("lce::gemm_f32out_kernel<A MN-contig, B MN-contig>", "bwd", B.LCE_STEP_DWEIGHT),
+        "strip_lse": "lce::strip_lse_kernel",
+        "merge": "lce::fold_kernel",
+        "strip_grad": "lce::strip_grad_kernel",
+        "gemm_dh": "lce::gemm_f32out_kernel<A K-contig, B MN-contig>",
+        "gemm_dw": "lce::gemm_f32out_kernel<A MN-contig, B MN-contig>",
+        "gemm_dh_dw": "lce::gemm_dh_dw_kernel (dH and dW sharing one launch)",
     }
-    flops_per_row = {"strip_lse": 2.0, "strip_grad": 2.0, "gemm_dh": 2.0, "gemm_dw": 2.0}
+    # algorithmic FLOP per (token x vocabulary row) of each launch
+    flops_per_elem = {"strip_lse": 2.0 * w.hidden, "strip_grad": 2.0 * w.hidden,
+                      "gemm_dh": 2.0 * w.hidden, "gemm_dw": 2.0 * w.hidden,
+                      "gemm_dh_dw": 4.0 * w.hidden}
     recs = {k: [] for k in kernels}
 
     def ev():
@@ -237,33 +247,47 @@ def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, 
         e.record()
         return e
 
+    if w.shards:
+        fwd_ranges = order
+    else:
+        wide = B.lce_forward_fold_max(p)
+        fwd_ranges = [(v0, min(wide, w.vocab - v0)) for v0 in range(0, w.vocab, wide)]
+    launches = {vl: B.lce_backward_fold_gemm_launches(p, vl) for _, vl in order}
+    S_STRIP, S_MERGE = B.LCE_STEP_STRIP, B.LCE_STEP_MERGE
+    S_GRAD, S_DH, S_DW = B.LCE_STEP_GRAD, B.LCE_STEP_DHIDDEN, B.LCE_STEP_DWEIGHT
     for _ in range(args.steps):
         B.lce_forward_begin(p, ws)
-        for v0, vl in order:
-            for k in ("strip_lse", "merge"):
+        for v0, vl in fwd_ranges:
+            for k, st in (("strip_lse", S_STRIP), ("merge", S_MERGE)):
                 a = ev()
-                B.lce_forward_fold_steps(p, h, W[v0:v0 + vl], v0, vl, t, ws, kernels[k][2])
+                B.lce_forward_fold_steps(p, h, W[v0:v0 + vl], v0, vl, t, ws, st)
                 recs[k].append((a, ev(), vl))
         B.lce_forward_end(p, t, loss, lse, None, ws)
         B.lce_backward_begin(p, t, go, ws)
         for i, (v0, vl) in enumerate(order):
-            for k in ("strip_grad", "gemm_dh", "gemm_dw"):
+            parts = [("strip_grad", S_GRAD)]
+            parts += [("gemm_dh", S_DH), ("gemm_dw", S_DW)] if launches[vl] == 2 \
+                else [("gemm_dh_dw", S_DH | S_DW)]
+            for k, st in parts:
                 a = ev()
                 B.lce_backward_fold_steps(p, h, W[v0:v0 + vl], v0, vl, t, lse, dh, i > 0,
-                                          dw[v0:v0 + vl], ws, kernels[k][2])
+                                          dw[v0:v0 + vl], ws, st)
                 recs[k].append((a, ev(), vl))
     torch.cuda.synchronize()
     out = {}
     for k, lst in recs.items():
+        if not lst:
+            continue
         ms = [a.elapsed_time(b) for a, b, _ in lst]
-        entry = {"kernel": kernels[k][0], "launches": len(ms), "avg_ms": round(float(np.mean(ms)), 4),
+        entry = {"kernel": kernels[k], "launches_per_step": len(ms) // args.steps,
+                 "avg_ms": round(float(np.mean(ms)), 4),
                  "total_ms_per_step": round(float(np.sum(ms)) / args.steps, 3)}
-        if k in flops_per_row:
-            fl = sum(flops_per_row[k] * w.n_tokens * w.hidden * vl for _, _, vl in lst)
+        if k in flops_per_elem:
+            fl = sum(flops_per_elem[k] * w.n_tokens * vl for _, _, vl in lst)
             entry["tflops"] = round(fl / (np.sum(ms) * 1e-3) / 1e12, 2)
             entry["algorithmic_flop_per_launch"] = fl / len(ms)
         out[k] = entry
-    dom = max(flops_per_row, key=lambda k: out[k]["total_ms_per_step"])
+    dom = max((k for k in flops_per_elem if k in out), key=lambda k: out[k]["total_ms_per_step"])
     achieved = out[dom]["tflops"]
     roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, dom),
@@ -274,9 +298,40 @@ def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, 
     return out, roof
 
 
+def cpu_facts():
+    """CPU model, logical CPUs, physical cores (distinct package/core pairs) and
+    the CPUs this process may run on."""
+    model, pairs = None, set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None and core is not None:
+                    pairs.add((phys, core))
+                    phys = core = None
+        if phys is not None and core is not None:
+            pairs.add((phys, core))
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(),
+            "physical_cores": len(pairs) or None,
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(w, hid_np, wt, t_np, rows):
-    """The CPU oracle, as it is, on the first `rows` tokens with the full weight."""
-    from threadpoolctl import threadpool_info
+    """The CPU oracle, as it is, on the first `rows` tokens with the full weight,
+    on every thread of the host's BLAS pool; plus its single-thread rate on the
+    256-token float32 workload (whole problem), and the full workload's time
+    projected from the measured rate (labelled as a projection)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import lce_oracle as O
     from vocab_projection_amd import synthetic as S
@@ -289,11 +344,32 @@ def cpu_baseline(w, hid_np, wt, t_np, rows):
     sec = time.perf_counter() - t0
     flops = 8.0 * rows * w.hidden * w.vocab
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(flops / sec / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(sec, 2),
-            "sample": f"first {rows} of {w.n_tokens} tokens with the full weight "
-                      f"(H={w.hidden}, V={w.vocab}): oracle forward + backward in float64, "
-                      f"8*{rows}*H*V FLOP"}
+    rate = flops / sec
+
+    tiny = S.WORKLOADS["tiny_f32"]
+    th, tw, tt = S.hidden(tiny), S.weight(tiny), S.targets(tiny)
+    with threadpool_limits(limits=1):
+        reps, t1 = 0, time.perf_counter()
+        while reps < 3 or time.perf_counter() - t1 < 1.0:
+            O.forward(th, tw, tt, ignore_index=S.IGNORE_INDEX, reduction=tiny.reduction)
+            O.backward(th, tw, tt, ignore_index=S.IGNORE_INDEX, reduction=tiny.reduction)
+            reps += 1
+        st_sec = (time.perf_counter() - t1) / reps
+    out = {"value": round(rate / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle", "seconds": round(sec, 2),
+           "sample": f"first {rows} of {w.n_tokens} tokens with the full weight "
+                     f"(H={w.hidden}, V={w.vocab}): oracle forward + backward in float64, "
+                     f"8*{rows}*H*V FLOP, on {threads} BLAS threads",
+           "single_thread": {"value": round(tiny.flops / st_sec / 1e12, 5), "unit": "TFLOP/s",
+                             "sample": f"{tiny.name} whole (N={tiny.n_tokens}, H={tiny.hidden}, "
+                                       f"V={tiny.vocab}, float32 inputs), oracle forward + "
+                                       f"backward, 1 thread, {reps} runs",
+                             "seconds_per_run": round(st_sec, 4)},
+           "projected_full_workload_seconds": round(w.flops / rate, 1),
+           "projection": f"8*N*H*V of the whole workload ({w.flops:.4g} FLOP) over the "
+                         f"measured {threads}-thread rate; not measured"}
+    out.update(cpu_facts())
+    return out
 
 
 if __name__ == "__main__":

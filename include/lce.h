@@ -78,29 +78,52 @@ typedef struct lce_problem {
 /* Human-readable name of a status code (static storage). */
 const char* lce_status_string(lce_status_t s);
 
-/* Widest strip width Vs whose workspace fits in budget_bytes: a multiple of
- * 256 (the kernels' vocabulary tile), at least 256, at most V rounded up to
- * 256 and at most 2^21, then clamped to V.  Follows from the second page's section 3.5 (device
- * working sets fixed by the launch configuration, checkable before launch).
- * Returns -1 for an invalid problem. p->strip is ignored. */
+/* Widest strip width Vs whose workspace (lce_workspace_bytes of the problem
+ * with that strip) fits in budget_bytes: a multiple of 256 (the kernels'
+ * vocabulary tile), at most V rounded up to 256 and at most 2^21, then
+ * clamped to V.  The workspace counted is the whole of it - the backward's
+ * gradient strip, or, for a handful of tokens, the forward's partials and
+ * running state when they are larger, plus the header - so the returned
+ * width's workspace never exceeds the budget.  Returns -1 when not even a
+ * 256-wide strip fits, and for an invalid problem; p->strip is ignored.
+ * (A problem with strip = 0 then uses 256, or V if smaller, whatever its
+ * workspace.)  Follows from the second page's sections 3.5 and 6: a
+ * device's working set is fixed by the launch configuration and can be
+ * checked before launch. */
 int64_t lce_pick_strip(const lce_problem_t* p, size_t budget_bytes);
 
 /* Workspace bytes needed by every call below for problem p (with its strip,
  * or the default policy when p->strip == 0): one gradient strip of
  * N x round_up(Vs, 256) elements plus a 256-byte header (the forward keeps its
- * partials and running state inside the strip region).
+ * partials and running state inside the strip region; for a handful of tokens
+ * those are larger than the strip and set the size).  This is the extra
+ * device memory of the whole path: the second page's section 3.2 bounds the
+ * projection's working set by one logit strip instead of the N x V logits,
+ * and its section 2 asks that the bound hold in the backward pass too, which
+ * recomputes strips into this same region.
  * Returns 0 for an invalid problem. */
 size_t lce_workspace_bytes(const lce_problem_t* p);
 
+/* Widest vocabulary range one forward fold (lce_forward_fold and its steps
+ * call) may take: at least Vs, and as many rows as the workspace's partials
+ * hold beside the running state (8 bytes per token and 128 rows), at most
+ * 2^21 and at most V.  lce_forward folds in ranges of this width.  Returns -1
+ * for an invalid problem. */
+int64_t lce_forward_fold_max(const lce_problem_t* p);
+
 /* Forward: loss[0] (float32, device), lse[N] (log-sum-exp of every row,
  * needed by lce_backward) and, if row_loss != NULL, row_loss[N] (0 for
- * ignored rows).  The vocabulary is folded in natural order.  Equivalent to
- * lce_forward_begin + lce_forward_fold over consecutive strips +
- * lce_forward_end, except that one fold here may span several strips: the
- * forward keeps only 8 bytes of partial state per token and 128 vocabulary
- * rows, so the workspace holds those of about 32 strips (bf16; 64 for f32)
- * and each fold takes as many, up to 2^21 rows.  Results agree with the
- * strip-by-strip calls up to the order of floating-point operations. */
+ * ignored rows).  This is the forward half of the first page's Linear CE
+ * (section "Linear CE: Avoiding Materialization of Full Logits"): the loss of
+ * the vocabulary projection without the logits tensor.  The vocabulary is
+ * folded in natural order into the running per-token state of the second
+ * page's section 3.2 (max, sum of exponentials, target logit).  Equivalent to
+ * lce_forward_begin + lce_forward_fold over consecutive ranges of
+ * lce_forward_fold_max(p) rows + lce_forward_end: the forward keeps only 8
+ * bytes of partial state per token and 128 vocabulary rows, so the workspace
+ * holds those of about 32 strips (bf16; 64 for f32) and each fold takes as
+ * many.  Results agree with strip-by-strip calls up to the order of
+ * floating-point operations (the second page's section 2). */
 lce_status_t lce_forward(const lce_problem_t* p, const void* hidden, const void* weight,
                          const int32_t* targets, float* loss, float* lse, float* row_loss,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -108,7 +131,11 @@ lce_status_t lce_forward(const lce_problem_t* p, const void* hidden, const void*
 /* Backward: d_hidden [N, H] and d_weight [V, H] (float32, fully overwritten)
  * of grad_out[0] * loss.  lse is the forward's output; grad_out is a device
  * scalar.  Ignored rows get zero d_hidden rows and add nothing to d_weight.
- * Equivalent to lce_backward_begin + one lce_backward_fold per strip. */
+ * The second page's section 3.2: the backward recomputes each strip's logits
+ * and forms their gradient strip by strip (G = scale * (softmax - onehot),
+ * dH += G . W_strip, dW_strip = G^T . h), so the logit gradients never exist
+ * for the whole vocabulary either.  Equivalent to lce_backward_begin + one
+ * lce_backward_fold per strip of Vs rows in natural order. */
 lce_status_t lce_backward(const lce_problem_t* p, const void* hidden, const void* weight,
                           const int32_t* targets, const float* lse, const float* grad_out,
                           float* d_hidden, float* d_weight, void* workspace,
@@ -119,13 +146,15 @@ lce_status_t lce_backward(const lce_problem_t* p, const void* hidden, const void
  * second page's Ring-DTP (appendix C): any order that visits every vocabulary
  * row exactly once gives the same result up to rounding.  weight_strip points
  * at row v_begin of the weight (v_len rows of H elements), 1 <= v_len <= Vs
- * and 0 <= v_begin, v_begin + v_len <= V. */
+ * (backward) or lce_forward_fold_max(p) (forward), and
+ * 0 <= v_begin, v_begin + v_len <= V. */
 
 /* Reset the running per-token state (max = -inf, sum = 0, target logit = NaN). */
 lce_status_t lce_forward_begin(const lce_problem_t* p, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
-/* Fold the logits of vocabulary rows [v_begin, v_begin + v_len) into the state. */
+/* Fold the logits of vocabulary rows [v_begin, v_begin + v_len) into the
+ * state; v_len may be up to lce_forward_fold_max(p) (>= Vs) rows. */
 lce_status_t lce_forward_fold(const lce_problem_t* p, const void* hidden,
                               const void* weight_strip, int64_t v_begin, int64_t v_len,
                               const int32_t* targets, void* workspace, size_t workspace_bytes,
@@ -164,7 +193,11 @@ lce_status_t lce_forward_merge_state(const lce_problem_t* p, const float* state,
                                      size_t workspace_bytes, hipStream_t stream);
 
 /* Count the non-ignored rows and form the per-row gradient scale from the
- * device scalar grad_out (grad_out / n_valid for mean, grad_out for sum). */
+ * device scalar grad_out (grad_out / n_valid for mean, grad_out for sum),
+ * kept in the workspace header for the folds that follow.  This is the
+ * factor grad_out * d loss / d row_loss of the dense loss that the second
+ * page's section 2 asks the gradients to reproduce: a row whose target is
+ * ignore_index gets 0, and the mean divides by the non-ignored rows. */
 lce_status_t lce_backward_begin(const lce_problem_t* p, const int32_t* targets,
                                 const float* grad_out, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
@@ -212,6 +245,14 @@ typedef enum lce_step {
   LCE_STEP_DWEIGHT = 4,
   LCE_STEP_ALL = 7
 } lce_step_t;
+
+/* How a backward fold of v_len rows launches its two output GEMMs on the
+ * current device: 2 for two launches (d_hidden, then d_weight_strip), 1 for
+ * one launch that shares the compute units between them (taken when one of
+ * the two alone has too few tiles to fill the device).  Lets a caller that
+ * times each step match the launches the whole fold makes.  -1 for an
+ * invalid problem or v_len outside [1, Vs]. */
+int lce_backward_fold_gemm_launches(const lce_problem_t* p, int64_t v_len);
 
 lce_status_t lce_forward_fold_steps(const lce_problem_t* p, const void* hidden,
                                     const void* weight_strip, int64_t v_begin, int64_t v_len,

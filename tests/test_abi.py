@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(names) == sorted(B.EXPORTS)
@@ -67,7 +67,8 @@ def test_pick_strip_policy(lib):
     vs = B.lce_pick_strip(p, fixed + n * 2 * 8192)
     assert vs == 8192
     assert B.lce_pick_strip(p, fixed + n * 2 * 8192 - 1) == 8192 - 256
-    assert B.lce_pick_strip(p, 0) == 256          # floor: one tile
+    assert B.lce_pick_strip(p, 0) == -1           # not even one tile fits
+    assert B.lce_pick_strip(p, 256 + n * 2 * 256) == 256
     assert B.lce_pick_strip(p, 1 << 50) == 151936  # ceiling: the whole vocabulary
     for budget in (1 << 28, 1 << 30, 3 << 30):
         vs = B.lce_pick_strip(p, budget)
@@ -117,7 +118,16 @@ def test_errors_are_returned_before_any_launch(lib):
     assert lib.lce_forward_fold(ctypes.byref(p), fake, fake, 0, 0, fake, fake, need, None) == 1
     p.strip = 256
     need = B.lce_workspace_bytes(p)
-    assert lib.lce_forward_fold(ctypes.byref(p), fake, fake, 0, 257, fake, fake, need, None) == 1
+    wide = B.lce_forward_fold_max(p)   # the forward's partials capacity, here the whole V
+    assert wide == 1000
+    p.vocab = 1 << 20
+    wide = B.lce_forward_fold_max(p)
+    assert wide >= 256 and wide % 128 == 0
+    assert lib.lce_forward_fold(ctypes.byref(p), fake, fake, 0, wide + 1, fake, fake, need,
+                                None) == 1
+    assert lib.lce_backward_fold(ctypes.byref(p), fake, fake, 0, 257, fake, fake, fake, 0, fake,
+                                 fake, need, None) == 1
+    p.vocab = 1000
     assert lib.lce_backward_fold(ctypes.byref(p), fake, fake, 0, 10, fake, None, fake, 0, fake,
                                  fake, need, None) == 1
     assert lib.lce_forward_state(ctypes.byref(p), None, fake, need, None) == 1
@@ -130,3 +140,19 @@ def test_errors_are_returned_before_any_launch(lib):
                                      bad_bits, fake, fake, need, None) == 1
     assert lib.lce_backward(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, need,
                             None) == 1
+
+
+def test_pick_strip_counts_the_whole_workspace(lib):
+    """For a handful of tokens the forward's partials and running state, not
+    the gradient strip, set the workspace; the picked width must still fit."""
+    for n, v, budget in ((1, 1 << 20, 64 << 10), (3, 300000, 40 << 10), (17, 5000, 1 << 16)):
+        p = P(n, 64, v)
+        vs = B.lce_pick_strip(p, budget)
+        assert vs > 0
+        assert B.lce_workspace_bytes(P(n, 64, v, strip=vs)) <= budget
+        wider = min(vs + 256, v)
+        if wider > vs:
+            assert B.lce_workspace_bytes(P(n, 64, v, strip=wider)) > budget
+    # strip = 0 with nothing fitting the default budget still plans one tile
+    big = P(1 << 31, 8, 1000)
+    assert B.lce_workspace_bytes(big) == 256 + (1 << 31) * 256 * 2

@@ -56,8 +56,16 @@ def check(dtype, got, ref, what, loss=False):
         assert abs(got - ref) <= tol * abs(ref), (what, float(got), float(ref))
         return abs(got - ref) / abs(ref)
     if dtype == "f32":
+        # max|diff| / max|ref| over the tensor, and the same row by row
         err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
         assert err <= 1e-4, (what, err)
+        g2, r2 = np.atleast_2d(got), np.atleast_2d(ref)
+        scale = np.abs(r2).max(axis=1)
+        diff = np.abs(g2 - r2).max(axis=1)
+        assert not np.any(diff[scale == 0] != 0), (what, "zero row")
+        if np.any(scale > 0):
+            err_rows = float((diff[scale > 0] / scale[scale > 0]).max())
+            assert err_rows <= 1e-4, (what, "row by row", err_rows)
     else:
         err = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
         assert err <= 1e-2, (what, err)

@@ -43,6 +43,8 @@ _SIGNATURES = {
     "lce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lce_pick_strip": (_I64, [_P, _SZ]),
     "lce_workspace_bytes": (_SZ, [_P]),
+    "lce_forward_fold_max": (_I64, [_P]),
+    "lce_backward_fold_gemm_launches": (ctypes.c_int, [_P, _I64]),
     "lce_forward": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lce_backward": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lce_forward_begin": (ctypes.c_int, [_P, _VP, _SZ, _VP]),
@@ -114,6 +116,20 @@ def lce_workspace_bytes(p: Problem) -> int:
     n = int(load().lce_workspace_bytes(ctypes.byref(p)))
     if n == 0:
         raise LceError("invalid problem")
+    return n
+
+
+def lce_forward_fold_max(p: Problem) -> int:
+    n = int(load().lce_forward_fold_max(ctypes.byref(p)))
+    if n < 0:
+        raise LceError("invalid problem")
+    return n
+
+
+def lce_backward_fold_gemm_launches(p: Problem, v_len: int) -> int:
+    n = int(load().lce_backward_fold_gemm_launches(ctypes.byref(p), v_len))
+    if n < 0:
+        raise LceError("invalid problem or strip length")
     return n
 
 

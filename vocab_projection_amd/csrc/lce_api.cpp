@@ -60,8 +60,6 @@ size_t state_col_bytes(int64_t n) { return (size_t)round_up(4 * n, 256); }
 
 size_t partial_bytes(int64_t n, int64_t ldg) { return (size_t)n * (size_t)(ldg / kPartRows) * 8; }
 
-size_t fixed_bytes(int64_t) { return kHeader; }
-
 size_t bytes_for_strip(int64_t n, int64_t vs, size_t elt) {
   const int64_t ldg = round_up(vs, kStripTile);
   const size_t g = (size_t)n * (size_t)ldg * elt;                            // backward G strip
@@ -69,21 +67,28 @@ size_t bytes_for_strip(int64_t n, int64_t vs, size_t elt) {
   return kHeader + (g > fwd ? g : fwd);
 }
 
+// Widest strip (a multiple of the 256-row tile, at most V rounded up and at
+// most 2^21, then clamped to V) whose whole workspace - the larger of the
+// backward's gradient strip and the forward's partials plus running state,
+// and the header - fits in `budget`; -1 if not even one tile's does.
+// bytes_for_strip grows with the strip, so the widest fit is found by
+// bisection over the tile count.
 int64_t pick_strip(const lce_problem_t* p, size_t budget) {
   const size_t elt = elt_of(p->dtype);
   const int64_t n = p->n_tokens;
-  const int64_t vmax = round_up(p->vocab, kStripTile);
-  int64_t vs = kStripTile;
-  const size_t fixed = fixed_bytes(n);  // the strip region holds everything else
-  if (budget > fixed) {
-    const size_t per_tile = (size_t)n * (size_t)kStripTile * elt;
-    const int64_t tiles = (int64_t)((budget - fixed) / per_tile);
-    if (tiles * kStripTile > vs) vs = tiles * kStripTile;
+  int64_t hi = round_up(p->vocab, kStripTile);
+  if (hi > kMaxStrip) hi = kMaxStrip;
+  int64_t lo_t = 0, hi_t = hi / kStripTile;  // widest fitting tile count in [lo_t, hi_t]
+  while (lo_t < hi_t) {
+    const int64_t mid = (lo_t + hi_t + 1) / 2;
+    if (bytes_for_strip(n, mid * kStripTile, elt) <= budget)
+      lo_t = mid;
+    else
+      hi_t = mid - 1;
   }
-  if (vs > vmax) vs = vmax;
-  if (vs > kMaxStrip) vs = kMaxStrip;
-  if (vs > p->vocab) vs = p->vocab;
-  return vs;
+  if (lo_t == 0) return -1;
+  const int64_t vs = lo_t * kStripTile;
+  return vs > p->vocab ? p->vocab : vs;
 }
 
 lce_status_t make_plan(const lce_problem_t* p, Plan* pl) {
@@ -93,7 +98,13 @@ lce_status_t make_plan(const lce_problem_t* p, Plan* pl) {
   pl->N = p->n_tokens;
   pl->H = p->hidden;
   pl->V = p->vocab;
-  pl->Vs = p->strip ? p->strip : pick_strip(p, LCE_DEFAULT_BUDGET);
+  if (p->strip) {
+    pl->Vs = p->strip;
+  } else {
+    // the default budget, or one tile when not even that fits it
+    const int64_t vs = pick_strip(p, LCE_DEFAULT_BUDGET);
+    pl->Vs = vs > 0 ? vs : (p->vocab < kStripTile ? p->vocab : kStripTile);
+  }
   pl->ldg = round_up(pl->Vs, kStripTile);
   pl->dtype = p->dtype;
   pl->reduction = p->reduction;
@@ -136,10 +147,12 @@ Carve carve(const Plan& pl, void* ws) {
                b + pl.off_strip};
 }
 
+// A fold's vocabulary rows: at most max_len of them (the strip for the
+// backward, the forward's partials capacity for the forward), inside [0, V).
 lce_status_t check_strip(const Plan& pl, const void* weight_strip, int64_t v_begin,
-                         int64_t v_len) {
+                         int64_t v_len, int64_t max_len) {
   if (!weight_strip || !aligned(weight_strip)) return LCE_ERR_INVALID_VALUE;
-  if (v_len < 1 || v_len > pl.Vs || v_begin < 0 || v_begin > pl.V - v_len)
+  if (v_len < 1 || v_len > max_len || v_begin < 0 || v_begin > pl.V - v_len)
     return LCE_ERR_INVALID_VALUE;
   return LCE_OK;
 }
@@ -232,6 +245,20 @@ int64_t lce_pick_strip(const lce_problem_t* p, size_t budget_bytes) {
   return pick_strip(p, budget_bytes);
 }
 
+int64_t lce_forward_fold_max(const lce_problem_t* p) {
+  Plan pl;
+  if (make_plan(p, &pl) != LCE_OK) return -1;
+  return pl.fwd_chunk < pl.V ? pl.fwd_chunk : pl.V;
+}
+
+int lce_backward_fold_gemm_launches(const lce_problem_t* p, int64_t v_len) {
+  Plan pl;
+  if (make_plan(p, &pl) != LCE_OK || v_len < 1 || v_len > pl.Vs) return -1;
+  const int64_t split = pl.dtype == LCE_BF16 ? lce::dh_dw_split<__bf16>(v_len, pl.N, pl.H)
+                                             : lce::dh_dw_split<float>(v_len, pl.N, pl.H);
+  return split > 0 ? 1 : 2;
+}
+
 size_t lce_workspace_bytes(const lce_problem_t* p) {
   Plan pl;
   if (make_plan(p, &pl) != LCE_OK) return 0;
@@ -265,7 +292,7 @@ lce_status_t lce_forward_fold_steps(const lce_problem_t* p, const void* hidden,
   if (s != LCE_OK) return s;
   if ((s = check_ws(pl, ws, ws_bytes)) != LCE_OK) return s;
   if (!hidden || !aligned(hidden) || !targets) return LCE_ERR_INVALID_VALUE;
-  if ((s = check_strip(pl, weight_strip, v_begin, v_len)) != LCE_OK) return s;
+  if ((s = check_strip(pl, weight_strip, v_begin, v_len, pl.fwd_chunk)) != LCE_OK) return s;
   if (steps & ~(unsigned)(LCE_STEP_STRIP | LCE_STEP_MERGE)) return LCE_ERR_INVALID_VALUE;
   return pl.dtype == LCE_BF16
              ? fold_fwd<__bf16>(pl, hidden, weight_strip, v_begin, v_len, targets, ws, steps,
@@ -368,7 +395,7 @@ lce_status_t lce_backward_fold_steps(const lce_problem_t* p, const void* hidden,
   if (!hidden || !aligned(hidden) || !targets || !lse || !d_hidden || !d_weight_strip)
     return LCE_ERR_INVALID_VALUE;
   if (!aligned(d_hidden) || !aligned(d_weight_strip)) return LCE_ERR_INVALID_VALUE;
-  if ((s = check_strip(pl, weight_strip, v_begin, v_len)) != LCE_OK) return s;
+  if ((s = check_strip(pl, weight_strip, v_begin, v_len, pl.Vs)) != LCE_OK) return s;
   if (steps & ~(unsigned)LCE_STEP_ALL) return LCE_ERR_INVALID_VALUE;
   if (accumulate & ~(LCE_ACC_DHIDDEN | LCE_ACC_DWEIGHT)) return LCE_ERR_INVALID_VALUE;
   return pl.dtype == LCE_BF16

@@ -57,6 +57,10 @@ hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T
                         int64_t v_len, int64_t n_tok, int64_t h, float* d_hidden, int acc_dh,
                         float* d_weight_strip, int acc_dw, hipStream_t st);
 
+// Blocks of the shared launch that work on dH, or 0 when launch_dh_dw issues
+// two launches (dH, then dW) for a strip of v_len rows.
+template <typename T> int64_t dh_dw_split(int64_t v_len, int64_t n_tok, int64_t h);
+
 hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st);
 hipError_t launch_fold(const float2* partials, int64_t n_blocks, float* m, float* s, int64_t n,
                        hipStream_t st);

@@ -796,17 +796,15 @@ static int64_t stage_load(int64_t tiles, int64_t nk, int64_t blocks) {
   return cdiv(tiles, blocks) * nk;
 }
 
+// Blocks of a shared dH + dW launch that work on dH, or 0 for two launches:
+// the split (a multiple of 8) that minimises the longest block's stage count,
+// taken only when both GEMMs are persistent (more stages per tile than the
+// ring holds) and the shared launch is strictly shorter than two launches.
 template <typename T>
-hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T* hidden,
-                        int64_t v_len, int64_t n_tok, int64_t h, float* d_hidden, int acc_dh,
-                        float* d_weight_strip, int acc_dw, hipStream_t st) {
-  const GemmArgs<T> dh = dh_args(g_strip, ldg, w_strip, v_len, n_tok, h, d_hidden);
-  const GemmArgs<T> dw = dw_args(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip);
-  const int64_t t_dh = dh.m_tiles * dh.n_tiles, nk_dh = stages_of<T>(dh.k_len);
-  const int64_t t_dw = dw.m_tiles * dw.n_tiles, nk_dw = stages_of<T>(dw.k_len);
+int64_t dh_dw_split(int64_t v_len, int64_t n_tok, int64_t h) {
+  const int64_t t_dh = cdiv(n_tok, kTile) * cdiv(h, kTile), nk_dh = stages_of<T>(v_len);
+  const int64_t t_dw = cdiv(v_len, kTile) * cdiv(h, kTile), nk_dw = stages_of<T>(n_tok);
   const int64_t p = persistent_blocks();
-  // Both persistent (more stages per tile than the ring holds) and the shared
-  // launch strictly shorter than two launches: share; else two launches.
   int64_t best_split = 0, best = stage_load(t_dh, nk_dh, p) + stage_load(t_dw, nk_dw, p);
   if (nk_dh > kStages && nk_dw > kStages) {
     for (int64_t split = kXcds; split < p; split += kXcds) {
@@ -815,11 +813,22 @@ hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T
       if (c < best) { best = c; best_split = split; }
     }
   }
+  return best_split;
+}
+
+template <typename T>
+hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T* hidden,
+                        int64_t v_len, int64_t n_tok, int64_t h, float* d_hidden, int acc_dh,
+                        float* d_weight_strip, int acc_dw, hipStream_t st) {
+  const int64_t best_split = dh_dw_split<T>(v_len, n_tok, h);
   if (best_split == 0) {
     hipError_t e = launch_dh(g_strip, ldg, w_strip, v_len, n_tok, h, d_hidden, acc_dh, st);
     if (e != hipSuccess) return e;
     return launch_dw(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip, acc_dw, st);
   }
+  const GemmArgs<T> dh = dh_args(g_strip, ldg, w_strip, v_len, n_tok, h, d_hidden);
+  const GemmArgs<T> dw = dw_args(g_strip, ldg, hidden, v_len, n_tok, h, d_weight_strip);
+  const int64_t p = persistent_blocks();
   if (acc_dh)
     return acc_dw ? launch_dh_dw_shared<T, true, true>(dh, dw, best_split, p, st)
                   : launch_dh_dw_shared<T, true, false>(dh, dw, best_split, p, st);
@@ -885,5 +894,7 @@ template hipError_t launch_dh_dw<float>(const float*, int64_t, const float*, con
                                         int64_t, int64_t, float*, int, float*, int, hipStream_t);
 template hipError_t launch_dw<float>(const float*, int64_t, const float*, int64_t, int64_t,
                                      int64_t, float*, int, hipStream_t);
+template int64_t dh_dw_split<__bf16>(int64_t, int64_t, int64_t);
+template int64_t dh_dw_split<float>(int64_t, int64_t, int64_t);
 
 }  // namespace lce
