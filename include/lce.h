@@ -224,6 +224,28 @@ lce_status_t lce_backward_fold(const lce_problem_t* p, const void* hidden,
                                int accumulate, float* d_weight_strip, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Backward with no workspace argument ----
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): lce_backward with
+ * its workspace taken from a static device array of LCE_STATIC_SCRATCH_BYTES
+ * inside the library instead of the caller.  Each GPU the library runs on
+ * holds its own copy of that array from the first call on it until the
+ * process ends; the call itself allocates nothing.  Problems whose
+ * lce_workspace_bytes exceeds LCE_STATIC_SCRATCH_BYTES are rejected with
+ * LCE_ERR_WORKSPACE before anything is enqueued (choose a narrower strip,
+ * e.g. lce_pick_strip(p, LCE_STATIC_SCRATCH_BYTES)).  Every call on one GPU
+ * uses the same array: two calls that can overlap on one GPU (different
+ * streams, or different host threads) race and must be serialised by the
+ * caller.  The array keeps the previous call's contents; the backward writes
+ * every byte it reads, so nothing needs clearing.  LCE_ERR_LAUNCH also
+ * reports a failed lookup of the array's device address.  Arguments and
+ * results are otherwise those of lce_backward. */
+#define LCE_STATIC_SCRATCH_BYTES ((size_t)256 << 20) /* 256 MiB per GPU */
+
+lce_status_t lce_backward_static(const lce_problem_t* p, const void* hidden, const void* weight,
+                                 const int32_t* targets, const float* lse, const float* grad_out,
+                                 float* d_hidden, float* d_weight, hipStream_t stream);
+
 /* ---- The steps of one fold, one kernel each ----
  * lce_forward_fold and lce_backward_fold run every step of their fold in
  * order; the calls below run only the steps named in `steps` (a bit set of

@@ -53,6 +53,7 @@ _SIGNATURES = {
     "lce_forward_state": (ctypes.c_int, [_P, _VP, _VP, _SZ, _VP]),
     "lce_forward_merge_state": (ctypes.c_int, [_P, _VP, _VP, _SZ, _VP]),
     "lce_backward_begin": (ctypes.c_int, [_P, _VP, _VP, _VP, _SZ, _VP]),
+    "lce_backward_static": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "lce_backward_fold": (ctypes.c_int, [_P, _VP, _VP, _I64, _I64, _VP, _VP, _VP, ctypes.c_int,
                                          _VP, _VP, _SZ, _VP]),
     "lce_forward_fold_steps": (ctypes.c_int, [_P, _VP, _VP, _I64, _I64, _VP, _VP, _SZ,
@@ -144,6 +145,17 @@ def lce_backward(p, hidden, weight, targets, lse, grad_out, d_hidden, d_weight, 
     _check(load().lce_backward(ctypes.byref(p), _ptr(hidden), _ptr(weight), _ptr(targets),
                                _ptr(lse), _ptr(grad_out), _ptr(d_hidden), _ptr(d_weight),
                                _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+LCE_STATIC_SCRATCH_BYTES = 256 << 20
+
+
+def lce_backward_static(p, hidden, weight, targets, lse, grad_out, d_hidden, d_weight,
+                        stream=None):
+    """lce_backward with the library's static per-GPU workspace (no workspace argument)."""
+    _check(load().lce_backward_static(ctypes.byref(p), _ptr(hidden), _ptr(weight), _ptr(targets),
+                                      _ptr(lse), _ptr(grad_out), _ptr(d_hidden), _ptr(d_weight),
+                                      _stream(stream)))
 
 
 def lce_forward_begin(p, workspace, stream=None):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblce.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["lce_kernels.hip", "lce_api.cpp"]
+SOURCES = ["lce_kernels.hip", "lce_api.cpp", "lce_noalloc.hip"]
 ARCH = "gfx950"
 
 
