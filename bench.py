@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--strip", type=int, default=0,
                     help="strip width Vs instead of the workload's (natural fold order only)")
+    ap.add_argument("--backward", default="strip", choices=["strip", "one_sweep", "two_sweeps"],
+                    help="backward form: the strip path (lce_backward), or the backward "
+                         "without a strip buffer (lce_backward_fused) in one or two sweeps")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -75,7 +78,7 @@ def main():
     from vocab_projection_amd import binding as B
     from vocab_projection_amd import synthetic as S
 
-    w = S.WORKLOADS[args.workload]
+    w = S.WORKLOADS.get(args.workload) or S.EXTRA_WORKLOADS[args.workload]
     if args.strip:
         if w.shards:
             print("--strip applies to workloads folded in natural order", file=sys.stderr)
@@ -96,17 +99,29 @@ def main():
     log(f"inputs {w.name}: {time.time() - t0:.1f}s")
 
     p = B.make_problem(h, W, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, strip=w.strip)
+    order = S.fold_order(w)
+    natural = w.shards == 0
     ws = B.workspace(p, dev)
+    fused = args.backward != "strip"
+    if fused:
+        if not natural:
+            print("--backward applies to workloads folded in natural order", file=sys.stderr)
+            sys.exit(2)
+        fmode = B.FUSED_MODES[args.backward]
+        fws = torch.empty(B.lce_backward_fused_workspace_bytes(p, fmode), dtype=torch.uint8,
+                          device=dev)
+        args.no_breakdown = True
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     lse = torch.empty(w.n_tokens, dtype=torch.float32, device=dev)
     dh = torch.empty(h.shape, dtype=torch.float32, device=dev)
     dw = torch.empty(W.shape, dtype=torch.float32, device=dev)
     go = torch.tensor([w.grad_out], dtype=torch.float32, device=dev)
-    order = S.fold_order(w)
-    natural = w.shards == 0
 
     def step():
-        if natural:
+        if fused:
+            B.lce_forward(p, h, W, t, loss, lse, None, ws)
+            B.lce_backward_fused(p, h, W, t, lse, go, dh, dw, fmode, fws)
+        elif natural:
             B.lce_forward(p, h, W, t, loss, lse, None, ws)
             B.lce_backward(p, h, W, t, lse, go, dh, dw, ws)
         else:
@@ -162,10 +177,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "n_tokens": w.n_tokens, "hidden": w.hidden,
                    "vocab": w.vocab, "strip": w.strip, "reduction": w.reduction,
-                   "fold_order": "natural" if natural else f"ring of {w.shards} shards"},
+                   "fold_order": "natural" if natural else f"ring of {w.shards} shards",
+                   "backward": args.backward},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "memory": {
             "workspace_bytes": B.lce_workspace_bytes(p),
+            "backward_workspace_bytes": fws.numel() if fused else B.lce_workspace_bytes(p),
             "strip_bytes": w.n_tokens * w.strip * w.elt_bytes,
             "full_logits_bytes": w.n_tokens * w.vocab * w.elt_bytes,
             "allocator_peak_extra_bytes": int(peak_alloc_extra),

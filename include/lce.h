@@ -246,6 +246,41 @@ lce_status_t lce_backward_static(const lce_problem_t* p, const void* hidden, con
                                  const int32_t* targets, const float* lse, const float* grad_out,
                                  float* d_hidden, float* d_weight, hipStream_t stream);
 
+/* ---- Backward without a strip buffer ----
+ * The fused alternative that the second page's section 5 sets beside
+ * Ring-DTP (cross-entropy kernels that keep the logit gradient out of memory
+ * for a batch resident on one device): the gradient G is formed one
+ * 256 x 256 (token x vocabulary) tile at a time and multiplied at once into
+ * the rows of d_hidden and d_weight that tile feeds, so no strip of G exists.
+ * Each tile's logits are recomputed as in section 3.2 of that page.
+ *   LCE_FUSED_ONE_SWEEP: every tile is visited once and feeds both
+ *     gradients (6 N H V multiply-adds of the backward, as the strip path).
+ *     The device is shared out as a grid of token groups x vocabulary groups;
+ *     each group's contribution goes to its own fp32 partial copy of d_hidden
+ *     (one per vocabulary group) and of d_weight (one per token group), and
+ *     the copies are summed in a fixed order afterwards.
+ *   LCE_FUSED_TWO_SWEEPS: a first sweep forms d_hidden with each token group
+ *     owning its rows, a second sweep recomputes every tile and forms
+ *     d_weight with each vocabulary group owning its rows (8 N H V: the
+ *     logits are formed twice), so partial copies appear only when the
+ *     device has more compute units than a dimension has tiles.
+ * Both are deterministic (fixed order of additions, no atomics).  The
+ * workspace is lce_backward_fused_workspace_bytes(p, mode): a 256-byte
+ * header, one G tile per block (128 KiB for bf16) and the partial copies.
+ * Arguments and results are otherwise those of lce_backward; H must be a
+ * multiple of 4.  The strip path (lce_backward) stays the default: its
+ * workspace is one strip, and at the pages' sizes the partial copies of the
+ * one-sweep form exceed it (they grow with H, a strip does not). */
+typedef enum lce_fused_mode { LCE_FUSED_ONE_SWEEP = 1, LCE_FUSED_TWO_SWEEPS = 2 } lce_fused_mode_t;
+
+/* Workspace bytes of lce_backward_fused for problem p and mode; 0 if invalid. */
+size_t lce_backward_fused_workspace_bytes(const lce_problem_t* p, int mode);
+
+lce_status_t lce_backward_fused(const lce_problem_t* p, const void* hidden, const void* weight,
+                                const int32_t* targets, const float* lse, const float* grad_out,
+                                float* d_hidden, float* d_weight, int mode, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* ---- The steps of one fold, one kernel each ----
  * lce_forward_fold and lce_backward_fold run every step of their fold in
  * order; the calls below run only the steps named in `steps` (a bit set of

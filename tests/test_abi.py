@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(names) == sorted(B.EXPORTS)
@@ -156,3 +156,23 @@ def test_pick_strip_counts_the_whole_workspace(lib):
     # strip = 0 with nothing fitting the default budget still plans one tile
     big = P(1 << 31, 8, 1000)
     assert B.lce_workspace_bytes(big) == 256 + (1 << 31) * 256 * 2
+
+
+def test_fused_backward_workspace_plan(lib):
+    """The strip-free backward's workspace: header + one 256 x 256 G tile per
+    block + fp32 partial copies.  Two sweeps at 131072 tokens and 151936 rows
+    need no partial copies (both dimensions have more tiles than the 256
+    blocks); one sweep needs copies of d_hidden and d_weight that grow with H."""
+    p = P(131072, 2048, 151936, strip=8192)
+    two = B.lce_backward_fused_workspace_bytes(p, B.LCE_FUSED_TWO_SWEEPS)
+    assert two == 256 + 256 * 256 * 256 * 2
+    one = B.lce_backward_fused_workspace_bytes(p, B.LCE_FUSED_ONE_SWEEP)
+    assert one > 10 * B.lce_workspace_bytes(p)
+    small = P(4096, 512, 32768, strip=8192)
+    for mode in (B.LCE_FUSED_ONE_SWEEP, B.LCE_FUSED_TWO_SWEEPS):
+        n = B.lce_backward_fused_workspace_bytes(small, mode)
+        assert n > 256 and (n - 256) % 256 == 0
+    assert lib.lce_backward_fused_workspace_bytes(ctypes.byref(p), 3) == 0
+    fake = 0x10000
+    assert lib.lce_backward_fused(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, 1,
+                                  fake, one - 1, None) == 3

@@ -45,6 +45,9 @@ _SIGNATURES = {
     "lce_workspace_bytes": (_SZ, [_P]),
     "lce_forward_fold_max": (_I64, [_P]),
     "lce_backward_fold_gemm_launches": (ctypes.c_int, [_P, _I64]),
+    "lce_backward_fused_workspace_bytes": (_SZ, [_P, ctypes.c_int]),
+    "lce_backward_fused": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int,
+                                          _VP, _SZ, _VP]),
     "lce_forward": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lce_backward": (ctypes.c_int, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "lce_forward_begin": (ctypes.c_int, [_P, _VP, _SZ, _VP]),
@@ -220,6 +223,25 @@ def lce_backward_fold_steps(p, hidden, weight_strip, v_begin, v_len, targets, ls
                                           _ptr(d_hidden), _acc_bits(accumulate, accumulate_dw),
                                           _ptr(d_weight_strip), _ptr(workspace),
                                           workspace.numel(), steps, _stream(stream)))
+
+
+LCE_FUSED_ONE_SWEEP, LCE_FUSED_TWO_SWEEPS = 1, 2
+FUSED_MODES = {"one_sweep": LCE_FUSED_ONE_SWEEP, "two_sweeps": LCE_FUSED_TWO_SWEEPS}
+
+
+def lce_backward_fused_workspace_bytes(p: Problem, mode: int) -> int:
+    n = int(load().lce_backward_fused_workspace_bytes(ctypes.byref(p), mode))
+    if n == 0:
+        raise LceError("invalid problem or mode")
+    return n
+
+
+def lce_backward_fused(p, hidden, weight, targets, lse, grad_out, d_hidden, d_weight, mode,
+                       workspace, stream=None):
+    """The backward without a strip buffer (mode LCE_FUSED_ONE_SWEEP or _TWO_SWEEPS)."""
+    _check(load().lce_backward_fused(ctypes.byref(p), _ptr(hidden), _ptr(weight), _ptr(targets),
+                                     _ptr(lse), _ptr(grad_out), _ptr(d_hidden), _ptr(d_weight),
+                                     mode, _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 LCE_ACC_NONE, LCE_ACC_DHIDDEN, LCE_ACC_DWEIGHT = 0, 1, 2

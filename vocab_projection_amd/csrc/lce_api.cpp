@@ -225,6 +225,119 @@ lce_status_t fold_bwd(const Plan& pl, const void* hidden, const void* weight_str
   return s;
 }
 
+// ---- The backward without a strip buffer ----
+constexpr int64_t kFusedBlocks = 256;  // blocks a fused sweep aims for (one per compute unit)
+
+struct FusedSweep {
+  int64_t C, R, tok_per_r, voc_per_c;
+  int do_dh, do_dw;
+  int64_t blocks() const { return C * R; }
+};
+
+struct FusedPlan {
+  FusedSweep sweep[2];
+  int n_sweeps;
+  size_t off_g, off_parts, total;
+};
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Groups of `tiles` tiles so that `groups` <= want: (groups, tiles per group).
+void split_groups(int64_t tiles, int64_t want, int64_t* groups, int64_t* per) {
+  if (want < 1) want = 1;
+  *per = cdiv64(tiles, want < tiles ? want : tiles);
+  *groups = cdiv64(tiles, *per);
+}
+
+size_t sweep_partials(const Plan& pl, const FusedSweep& sw) {
+  size_t b = 0;
+  if (sw.do_dh && sw.C > 1) b += (size_t)sw.C * pl.N * pl.H * 4;
+  if (sw.do_dw && sw.R > 1) b += (size_t)sw.R * pl.V * pl.H * 4;
+  return b;
+}
+
+lce_status_t make_fused_plan(const Plan& pl, int mode, FusedPlan* fp) {
+  const int64_t tt = cdiv64(pl.N, kStripTile), vt = cdiv64(pl.V, kStripTile);
+  if (mode == LCE_FUSED_ONE_SWEEP) {
+    // one sweep over all pairs, both outputs: the token x vocabulary grid of
+    // groups with the least partial memory among those that fill the device
+    FusedSweep best{};
+    size_t best_bytes = (size_t)-1;
+    const int64_t need = tt * vt < kFusedBlocks ? tt * vt : kFusedBlocks;
+    for (int64_t r_want = 1; r_want <= (tt < kFusedBlocks ? tt : kFusedBlocks); ++r_want) {
+      FusedSweep sw{};
+      sw.do_dh = sw.do_dw = 1;
+      split_groups(tt, r_want, &sw.R, &sw.tok_per_r);
+      split_groups(vt, cdiv64(kFusedBlocks, sw.R), &sw.C, &sw.voc_per_c);
+      if (sw.blocks() < need && sw.R * sw.C < tt * vt) continue;
+      const size_t b = sweep_partials(pl, sw);
+      if (b < best_bytes) { best_bytes = b; best = sw; }
+    }
+    fp->sweep[0] = best;
+    fp->n_sweeps = 1;
+  } else if (mode == LCE_FUSED_TWO_SWEEPS) {
+    // sweep 1: dH, a block per token group (vocabulary split only if there
+    // are too few token tiles); sweep 2: dW, a block per vocabulary group
+    FusedSweep a{}, b{};
+    a.do_dh = 1;
+    split_groups(tt, kFusedBlocks, &a.R, &a.tok_per_r);
+    split_groups(vt, kFusedBlocks / a.R, &a.C, &a.voc_per_c);
+    b.do_dw = 1;
+    split_groups(vt, kFusedBlocks, &b.C, &b.voc_per_c);
+    split_groups(tt, kFusedBlocks / b.C, &b.R, &b.tok_per_r);
+    fp->sweep[0] = a;
+    fp->sweep[1] = b;
+    fp->n_sweeps = 2;
+  } else {
+    return LCE_ERR_INVALID_VALUE;
+  }
+  int64_t blocks = 0;
+  size_t parts = 0;
+  for (int k = 0; k < fp->n_sweeps; ++k) {
+    if (fp->sweep[k].blocks() > blocks) blocks = fp->sweep[k].blocks();
+    const size_t b = sweep_partials(pl, fp->sweep[k]);
+    if (b > parts) parts = b;
+  }
+  fp->off_g = kHeader;
+  fp->off_parts = fp->off_g + (size_t)round_up((int64_t)blocks * kStripTile * kStripTile * pl.elt, 256);
+  fp->total = fp->off_parts + parts;
+  return LCE_OK;
+}
+
+template <typename T>
+lce_status_t fused_backward(const Plan& pl, const FusedPlan& fp, const void* hidden,
+                            const void* weight, const int32_t* targets, const float* lse,
+                            float* d_hidden, float* d_weight, void* ws, hipStream_t st) {
+  char* b = static_cast<char*>(ws);
+  float* parts = reinterpret_cast<float*>(b + fp.off_parts);
+  for (int k = 0; k < fp.n_sweeps; ++k) {
+    const FusedSweep& sw = fp.sweep[k];
+    lce::FusedLaunch<T> L{};
+    L.hidden = static_cast<const T*>(hidden);
+    L.weight = static_cast<const T*>(weight);
+    L.targets = targets;
+    L.lse = lse;
+    L.ctrl = reinterpret_cast<const lce::Control*>(b);
+    L.N = pl.N; L.H = pl.H; L.V = pl.V;
+    L.ignore_index = pl.ignore_index;
+    L.g_scratch = reinterpret_cast<T*>(b + fp.off_g);
+    L.C = sw.C; L.R = sw.R; L.tok_per_r = sw.tok_per_r; L.voc_per_c = sw.voc_per_c;
+    L.do_dh = sw.do_dh; L.do_dw = sw.do_dw;
+    const bool dh_parts = sw.do_dh && sw.C > 1, dw_parts = sw.do_dw && sw.R > 1;
+    L.dh_dst = dh_parts ? parts : d_hidden;
+    L.dw_dst = dw_parts ? parts + (dh_parts ? (size_t)sw.C * pl.N * pl.H : 0) : d_weight;
+    lce_status_t s = launched(lce::launch_fused_bwd<T>(L, st));
+    if (s != LCE_OK) return s;
+    if (dh_parts && (s = launched(lce::launch_sum_parts(L.dh_dst, sw.C, pl.N * pl.H, d_hidden,
+                                                        st))) != LCE_OK)
+      return s;
+    if (dw_parts && (s = launched(lce::launch_sum_parts(L.dw_dst, sw.R, pl.V * pl.H, d_weight,
+                                                        st))) != LCE_OK)
+      return s;
+  }
+  return LCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -427,6 +540,39 @@ lce_status_t lce_backward(const lce_problem_t* p, const void* hidden, const void
     if (s != LCE_OK) return s;
   }
   return LCE_OK;
+}
+
+size_t lce_backward_fused_workspace_bytes(const lce_problem_t* p, int mode) {
+  Plan pl;
+  FusedPlan fp;
+  if (make_plan(p, &pl) != LCE_OK || make_fused_plan(pl, mode, &fp) != LCE_OK) return 0;
+  return fp.total;
+}
+
+lce_status_t lce_backward_fused(const lce_problem_t* p, const void* hidden, const void* weight,
+                                const int32_t* targets, const float* lse, const float* grad_out,
+                                float* d_hidden, float* d_weight, int mode, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  Plan pl;
+  lce_status_t s = make_plan(p, &pl);
+  if (s != LCE_OK) return s;
+  FusedPlan fp;
+  if ((s = make_fused_plan(pl, mode, &fp)) != LCE_OK) return s;
+  if (!ws || !aligned(ws) || ws_bytes < fp.total) return LCE_ERR_WORKSPACE;
+  if (!hidden || !weight || !targets || !lse || !grad_out || !d_hidden || !d_weight)
+    return LCE_ERR_INVALID_VALUE;
+  if (!aligned(hidden) || !aligned(weight) || !aligned(d_hidden) || !aligned(d_weight))
+    return LCE_ERR_INVALID_VALUE;
+  if (pl.H % 4 != 0) return LCE_ERR_UNSUPPORTED;  // the partial sums move 4 floats at a time
+  Carve c = carve(pl, ws);
+  if ((s = launched(lce::launch_grad_scale(targets, pl.N, pl.ignore_index, pl.reduction, grad_out,
+                                           c.ctrl, stream))) != LCE_OK)
+    return s;
+  return pl.dtype == LCE_BF16
+             ? fused_backward<__bf16>(pl, fp, hidden, weight, targets, lse, d_hidden, d_weight, ws,
+                                      stream)
+             : fused_backward<float>(pl, fp, hidden, weight, targets, lse, d_hidden, d_weight, ws,
+                                     stream);
 }
 
 }  // extern "C"

@@ -61,6 +61,30 @@ hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T
 // two launches (dH, then dW) for a strip of v_len rows.
 template <typename T> int64_t dh_dw_split(int64_t v_len, int64_t n_tok, int64_t h);
 
+// The backward without a strip buffer (fused_bwd_kernel): a grid of C x R
+// blocks, block r * C + c taking token tiles [r tok_per_r, + tok_per_r) and
+// vocabulary tiles [c voc_per_c, + voc_per_c); dH partials per vocabulary
+// group at dh_dst + c N H, dW partials per token group at dw_dst + r V H.
+template <typename T>
+struct FusedLaunch {
+  const T* hidden;
+  const T* weight;
+  const int32_t* targets;
+  const float* lse;
+  const Control* ctrl;
+  int64_t N, H, V;
+  int32_t ignore_index;
+  T* g_scratch;  // C R blocks x 256 x 256 elements
+  float* dh_dst;
+  float* dw_dst;
+  int64_t C, R, tok_per_r, voc_per_c;
+  int do_dh, do_dw;
+};
+template <typename T> hipError_t launch_fused_bwd(const FusedLaunch<T>& L, hipStream_t st);
+// out[k] = sum over p of parts[p * count + k], p in order; count % 4 == 0.
+hipError_t launch_sum_parts(const float* parts, int64_t P, int64_t count, float* out,
+                            hipStream_t st);
+
 hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st);
 hipError_t launch_fold(const float2* partials, int64_t n_blocks, float* m, float* s, int64_t n,
                        hipStream_t st);

@@ -155,9 +155,26 @@ template <typename T> struct GradStage {
   static_assert(kTok * kStride <= kStagingBytes, "staging fits in LDS");
 };
 
+// Where a tile's G goes: the element (token n0, vocabulary row m0) of the tile
+// at `tile`, rows `ld` elements apart, `bytes` valid bytes from there (rows
+// past them are dropped by the buffer's range check).
+template <typename T>
+struct GradDst {
+  T* tile;
+  int64_t ld;
+  int64_t bytes;
+};
+
+// The tile's place in the strip buffer G [N, ldg].
+template <typename T>
+__device__ __forceinline__ GradDst<T> strip_dst(const StripArgs<T>& a, int64_t m0, int64_t n0) {
+  return GradDst<T>{a.g_strip + n0 * a.ldg + m0, a.ldg,
+                    (a.N - n0) * a.ldg * (int64_t)sizeof(T) - m0 * (int64_t)sizeof(T)};
+}
+
 template <typename T>
 __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, int64_t m0,
-                                              int64_t n0, char* lds) {
+                                              int64_t n0, char* lds, const GradDst<T>& dst) {
   typedef GradStage<T> S;
   const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
   const int lane = tid & 63;
@@ -166,11 +183,10 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
   const int64_t vrow0 = m0 + wm * kWaveM;
   const bool full = vrow0 + kWaveM <= a.v_len;  // no strip rows past v_len in this wave
   const float scale_all = a.ctrl->grad_scale;
-  // G rows n0.. of the strip buffer from column m0: byte offset
-  // (tok - n0) * ldg * elt + (col - m0) * elt; rows past N are out of range.
-  const int64_t row_bytes = a.ldg * (int64_t)sizeof(T);
-  const __amdgpu_buffer_rsrc_t gbuf = make_buffer(
-      a.g_strip + n0 * a.ldg + m0, (a.N - n0) * row_bytes - m0 * (int64_t)sizeof(T));
+  // G rows of the tile: byte offset (tok - n0) * ld * elt + (col - m0) * elt;
+  // rows past the destination's valid bytes are out of range.
+  const int64_t row_bytes = dst.ld * (int64_t)sizeof(T);
+  const __amdgpu_buffer_rsrc_t gbuf = make_buffer(dst.tile, dst.bytes);
   static_assert(S::kTok <= kWaveN && kWaveN % S::kTok == 0, "a pass lies in one wave column");
   constexpr int kNiPerPass = S::kTok / kMfma;
 
@@ -242,7 +258,7 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<T>& a, Acc& acc, i
 // every copy and store in flight.)  Targets and lse are loaded before any
 // store, so waiting for them never waits for this tile's stores.
 __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& acc, int64_t m0,
-                                              int64_t n0, char* lds) {
+                                              int64_t n0, char* lds, const GradDst<__bf16>& dst) {
   constexpr int kRowBytes = kTile * 2;        // 256 bf16 vocabulary columns
   constexpr int kNiPass = 2;                  // column blocks per wave per pass
   constexpr int kPassTok = kWaves / 2 * kNiPass * kMfma;  // 128 tokens per pass
@@ -279,11 +295,10 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
     any_hit[ni] = __any(hit);
   }
 
-  // G rows n0.. of the strip buffer from column m0: byte offset
-  // (tok - n0) * ldg * 2 + (col - m0) * 2; rows past N are out of range.
-  const int64_t row_bytes = a.ldg * 2;
-  const __amdgpu_buffer_rsrc_t gbuf =
-      make_buffer(a.g_strip + n0 * a.ldg + m0, (a.N - n0) * row_bytes - m0 * 2);
+  // G rows of the tile: byte offset (tok - n0) * ld * 2 + (col - m0) * 2;
+  // rows past the destination's valid bytes are out of range.
+  const int64_t row_bytes = dst.ld * 2;
+  const __amdgpu_buffer_rsrc_t gbuf = make_buffer(dst.tile, dst.bytes);
 #pragma unroll
   for (int pass = 0; pass < kNI / kNiPass; ++pass) {
     block_barrier();  // staging free: the previous pass (or tile) is done with it
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
   const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
   run_tiles<T, true, true>(A, B, a.H, grid, lds,
                            [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
-                             grad_epilogue(a, acc, m0, n0, staging);
+                             grad_epilogue(a, acc, m0, n0, staging, strip_dst(a, m0, n0));
                            });
 }
 
@@ -490,6 +505,149 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dh_dw_kernel(GemmArgs<T> dh,
                                  gemm_epilogue<T, AccumDw>(dw, acc, m0, n0, staging);
                                });
   }
+}
+
+// ---------------------------------------------------------------------------
+// Backward without a strip buffer: each (token tile i, vocabulary tile j)
+// pair is recomputed, its G tile formed and multiplied at once into the rows
+// of dH and dW it feeds, so G never exists beyond one tile per block.
+// ---------------------------------------------------------------------------
+// Block b = r * C + c takes the pairs (i, j) with i in token group r and j in
+// vocabulary group c, i-major.  Per pair:
+//   Z^T = W_j . h_i^T (K = H), G = scale (softmax - onehot) into the block's
+//   own 256 x 256 tile of g_scratch;
+//   dh (with do_dh): dh_dst[c][rows of i] (+)= G . W_j   (K = rows of j)
+//   dw (with do_dw): dw_dst[r][rows of j] (+)= G^T . h_i (K = rows of i)
+// dh_dst[c] is written only by blocks of vocabulary group c and token rows of
+// their own token group, so each output row has one writer and a fixed order
+// of additions (over j for dH, over i for dW): no atomics, and results that do
+// not depend on timing.  The first pair that touches a row overwrites it.
+template <typename T>
+struct FusedArgs {
+  const T* hidden;         // [N, H]
+  const T* weight;         // [V, H]
+  const int32_t* targets;  // [N]
+  const float* lse;        // [N]
+  const Control* ctrl;
+  int64_t N, H, V;
+  int32_t ignore_index;
+  T* g_scratch;            // [gridDim.x][256][256]
+  float* dh_dst;           // [C][N][H] (dH itself when C == 1)
+  float* dw_dst;           // [R][V][H] (dW itself when R == 1)
+  int64_t C, tok_per_r, voc_per_c;  // groups: tiles per token group / vocabulary group
+  int do_dh, do_dw;
+};
+
+// C[0:m, 0:n] (+)= A . B^T for one block, its 256 x 256 output tiles walked
+// along n.  The persistent tile loop runs its copy stream one tile ahead, which
+// needs more K stages per tile than the ring holds; shorter K goes one tile
+// per call.
+template <typename T, bool AK, bool BK>
+__device__ __forceinline__ void block_gemm_rows(const Operand<T>& A, Operand<T> B, int64_t k_len,
+                                                GemmArgs<T> g, bool accum, char* lds) {
+  constexpr int64_t kStageK = kStageRowBytes / sizeof(T);
+  const int64_t n_tiles = (g.n + kTile - 1) / kTile;
+  auto epi = [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
+    if (accum)
+      gemm_epilogue<T, true>(g, acc, m0, n0, staging);
+    else
+      gemm_epilogue<T, false>(g, acc, m0, n0, staging);
+  };
+  if ((k_len + kStageK - 1) / kStageK > kStages) {
+    const TileGrid grid{1, n_tiles, 1, 0, 1, false};
+    run_tiles<T, AK, BK>(A, B, k_len, grid, lds, epi);
+    return;
+  }
+  const TileGrid one{1, 1, 1, 0, 1, false};
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    // B is MN-contiguous here: column block t starts t * 256 elements along a row
+    Operand<T> Bt{B.base + t * kTile, B.ld, B.mn_ext - t * kTile, B.k_ext};
+    GemmArgs<T> gt = g;
+    gt.c = g.c + t * kTile;
+    gt.n = g.n - t * kTile;
+    auto epi_t = [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
+      if (accum)
+        gemm_epilogue<T, true>(gt, acc, m0, n0, staging);
+      else
+        gemm_epilogue<T, false>(gt, acc, m0, n0, staging);
+    };
+    run_tiles<T, AK, BK>(A, Bt, k_len, one, lds, epi_t);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs<T> f) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int64_t b = blockIdx.x;
+  const int64_t c = b % f.C, r = b / f.C;
+  const int64_t tok_tiles = (f.N + kTile - 1) / kTile, voc_tiles = (f.V + kTile - 1) / kTile;
+  const int64_t i_lo = r * f.tok_per_r, i_hi = min(tok_tiles, i_lo + f.tok_per_r);
+  const int64_t j_lo = c * f.voc_per_c, j_hi = min(voc_tiles, j_lo + f.voc_per_c);
+  T* const gt = f.g_scratch + b * (int64_t)kTile * kTile;
+  // this block's copy of each output (the output itself when not split)
+  float* const dh = f.do_dh ? f.dh_dst + c * f.N * f.H : nullptr;
+  float* const dw = f.do_dw ? f.dw_dst + r * f.V * f.H : nullptr;
+  for (int64_t i = i_lo; i < i_hi; ++i) {
+    const int64_t t0 = i * kTile, nt = min<int64_t>(kTile, f.N - t0);
+    for (int64_t j = j_lo; j < j_hi; ++j) {
+      const int64_t v0 = j * kTile, nv = min<int64_t>(kTile, f.V - v0);
+      // the pair's logits, recomputed, and its G tile
+      StripArgs<T> a{};
+      a.hidden = f.hidden + t0 * f.H;
+      a.weight_strip = f.weight + v0 * f.H;
+      a.targets = f.targets + t0;
+      a.N = nt;
+      a.H = f.H;
+      a.v_begin = v0;
+      a.v_len = nv;
+      a.ignore_index = f.ignore_index;
+      a.lse = f.lse + t0;
+      a.ctrl = f.ctrl;
+      const Operand<T> Wj{a.weight_strip, f.H, nv, f.H};
+      const Operand<T> hi{a.hidden, f.H, nt, f.H};
+      const GradDst<T> dst{gt, kTile, nt * kTile * (int64_t)sizeof(T)};
+      run_tiles<T, true, true>(Wj, hi, f.H, TileGrid{1, 1, 1, 0, 1, false}, lds,
+                               [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
+                                 grad_epilogue(a, acc, m0, n0, staging, dst);
+                               });
+      // G's stores complete and are visible to the block's copies that follow
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      block_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (f.do_dh) {
+        // dH rows of tile i (+)= G[nt, nv] . W_j[nv, H]: A = G K-contiguous, B = W_j
+        // MN-contiguous (row = vocabulary row, the contraction index)
+        const Operand<T> A{gt, kTile, nt, nv};
+        const Operand<T> B{a.weight_strip, f.H, f.H, nv};
+        GemmArgs<T> g{};
+        g.c = dh + t0 * f.H; g.ldc = f.H; g.m = nt; g.n = f.H;
+        block_gemm_rows<T, true, false>(A, B, nv, g, j > j_lo, lds);
+      }
+      if (f.do_dw) {
+        // dW rows of tile j (+)= G^T[nv, nt] . h_i[nt, H]: both MN-contiguous (row =
+        // token, the contraction index); G's pad columns are zero
+        const int64_t cols = (nv + 7) / 8 * 8;
+        const Operand<T> A{gt, kTile, cols, nt};
+        const Operand<T> B{a.hidden, f.H, f.H, nt};
+        GemmArgs<T> g{};
+        g.c = dw + v0 * f.H; g.ldc = f.H; g.m = nv; g.n = f.H;
+        block_gemm_rows<T, false, false>(A, B, nt, g, i > i_lo, lds);
+      }
+      // every copy of G has landed before the next pair's epilogue rewrites it
+      block_barrier();
+    }
+  }
+}
+
+// out[k] = sum_p parts[p][k] over p = 0 .. P - 1 in that order (fixed order:
+// the result does not depend on timing).  count is a multiple of 4.
+__global__ void sum_parts_kernel(const float* __restrict__ parts, int64_t P, int64_t count,
+                                 float* __restrict__ out) {
+  const int64_t q = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (q >= count) return;
+  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(parts + q);
+  for (int64_t p = 1; p < P; ++p) acc += *reinterpret_cast<const f32x4_t*>(parts + p * count + q);
+  *reinterpret_cast<f32x4_t*>(out + q) = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -836,6 +994,31 @@ hipError_t launch_dh_dw(const T* g_strip, int64_t ldg, const T* w_strip, const T
                 : launch_dh_dw_shared<T, false, false>(dh, dw, best_split, p, st);
 }
 
+template <typename T>
+hipError_t launch_fused_bwd(const FusedLaunch<T>& L, hipStream_t st) {
+  FusedArgs<T> f{};
+  f.hidden = L.hidden; f.weight = L.weight; f.targets = L.targets; f.lse = L.lse;
+  f.ctrl = L.ctrl; f.N = L.N; f.H = L.H; f.V = L.V; f.ignore_index = L.ignore_index;
+  f.g_scratch = L.g_scratch;
+  f.dh_dst = L.dh_dst; f.dw_dst = L.dw_dst;
+  f.C = L.C; f.tok_per_r = L.tok_per_r; f.voc_per_c = L.voc_per_c;
+  f.do_dh = L.do_dh; f.do_dw = L.do_dw;
+  const int64_t blocks = L.C * L.R;
+  if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
+  hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&fused_bwd_kernel<T>));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fused_bwd_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, st, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_parts(const float* parts, int64_t P, int64_t count, float* out,
+                            hipStream_t st) {
+  const int64_t threads = cdiv(count, 4);
+  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st, parts,
+                     P, count, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_state_init(float* m, float* s, float* zt, int64_t n, hipStream_t st) {
   hipLaunchKernelGGL(state_init_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st, m, s, zt, n);
   return hipGetLastError();
@@ -895,6 +1078,8 @@ template hipError_t launch_dh_dw<float>(const float*, int64_t, const float*, con
 template hipError_t launch_dw<float>(const float*, int64_t, const float*, int64_t, int64_t,
                                      int64_t, float*, int, hipStream_t);
 template int64_t dh_dw_split<__bf16>(int64_t, int64_t, int64_t);
+template hipError_t launch_fused_bwd<__bf16>(const FusedLaunch<__bf16>&, hipStream_t);
+template hipError_t launch_fused_bwd<float>(const FusedLaunch<float>&, hipStream_t);
 template int64_t dh_dw_split<float>(int64_t, int64_t, int64_t);
 
 }  // namespace lce

@@ -88,9 +88,25 @@ WORKLOADS = {
         _w("bf16_n64k_h6k_v262k_ring8", 65536, 6144, 262144, 32768, "bf16", 1.0,
            20.0 / math.sqrt(6144), "zipf", zipf_s=1.1, ignore_frac=0.05, shards=8,
            ring_start=3, seed=1238),
+        # the second page's Ring-DTP benchmark shape (appendix C: N = 16384,
+        # H = 7168, V = 200000, FP32) as one device's whole problem; the page
+        # states no value distributions, so logits ~ N(0, 1): h ~ N(0, 1),
+        # W ~ N(0, 1/H), uniform targets, mean reduction
+        _w("f32_n16k_h7k_v200k", 16384, 7168, 200000, 8192, "f32", 1.0,
+           1.0 / math.sqrt(7168), "uniform", seed=1239),
     ]
 }
 WORKLOAD_ORDER = list(WORKLOADS)
+
+# Shapes measured beside the workloads above (their parity is covered by
+# dedicated small-shape tests): the strip-free backward's comparison shape.
+EXTRA_WORKLOADS = {
+    w.name: w
+    for w in [
+        _w("bf16_n4k_h512_v32k", 4096, 512, 32768, 8192, "bf16", 1.0, 0.02, "uniform",
+           ignore_frac=0.10, seed=1240),
+    ]
+}
 
 
 def _rng(*key: int) -> np.random.Generator:
