@@ -221,9 +221,11 @@ def kernel_source_sha256() -> str:
 
 
 def measured_traffic(workload: str, step: str):
-    """HBM bytes per launch of `step` from the committed FETCH_SIZE / WRITE_SIZE
-    summary (already scaled by the copy-kernel calibration), or None when there
-    is none for this workload or the kernels changed since it was taken."""
+    """Bytes per launch of `step` that leave the L2 caches towards memory, from
+    the committed FETCH_SIZE / WRITE_SIZE summary (scaled by the copy-kernel
+    calibration; MALL hits included, since no counter on this part separates
+    them from HBM), or None when there is none for this workload or the
+    kernels changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -232,7 +234,7 @@ def measured_traffic(workload: str, step: str):
     if prof.get("source_sha256") != kernel_source_sha256():
         return None
     k = prof.get("kernels", {}).get(step)
-    return None if k is None else k["hbm_bytes_per_dispatch"]
+    return None if k is None else k["l2_egress_bytes_per_dispatch"]
 
 
 def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, loss, peak):
@@ -308,6 +310,8 @@ def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, 
     achieved = out[dom]["tflops"]
     roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name, dom),
+            "traffic_counts": "bytes leaving L2 per launch (FETCH_SIZE + WRITE_SIZE, calibrated "
+                              "on a 1 GiB copy); MALL hits included",
             "kernel": out[dom]["kernel"],
             "step": dom, "avg_launch_ms": out[dom]["avg_ms"],
             "algorithmic_flop_per_launch": out[dom]["algorithmic_flop_per_launch"]}

@@ -94,7 +94,8 @@ int64_t lce_pick_strip(const lce_problem_t* p, size_t budget_bytes);
 
 /* Workspace bytes needed by every call below for problem p (with its strip,
  * or the default policy when p->strip == 0): one gradient strip of
- * N x round_up(Vs, 256) elements plus a 256-byte header (the forward keeps its
+ * round_up(N, 16) x round_up(Vs, 256) elements (bf16 strips are kept in
+ * blocks of 16 tokens) plus a 256-byte header (the forward keeps its
  * partials and running state inside the strip region; for a handful of tokens
  * those are larger than the strip and set the size).  This is the extra
  * device memory of the whole path: the second page's section 3.2 bounds the

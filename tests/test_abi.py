@@ -49,15 +49,20 @@ def P(n=64, h=64, v=1000, dtype=torch.bfloat16, **kw):
 
 
 def test_workspace_formula(lib):
-    """One strip of N x round_up(Vs, 256) elements plus a 256-byte header."""
+    """One strip of round_up(N, 16) x round_up(Vs, 256) elements plus a 256-byte
+    header (the strip buffer keeps whole 16-token bands)."""
     p = P(131072, 2048, 151936, strip=8192)
     assert B.lce_workspace_bytes(p) == 256 + 131072 * 8192 * 2
     p = P(256, 128, 1024, torch.float32, strip=256)
     assert B.lce_workspace_bytes(p) == 256 + 256 * 256 * 4
-    p = P(100, 64, 1000, strip=300)  # strip buffer rounds the strip up to 256 columns
-    assert B.lce_workspace_bytes(p) == 256 + 100 * 512 * 2
-    p = P(1, 8, 1, strip=1)  # one token: the forward's partials + state (16 + 3*256) win
-    assert B.lce_workspace_bytes(p) == 256 + 16 + 3 * 256
+    p = P(100, 64, 1000, strip=300)  # 256-column tiles, 16-token bands
+    assert B.lce_workspace_bytes(p) == 256 + 112 * 512 * 2
+    p = P(1, 8, 1, strip=1)  # one token: one band of one tile
+    assert B.lce_workspace_bytes(p) == 256 + 16 * 256 * 2
+    # three tokens, a million vocabulary rows: the forward's partials and state
+    # still fit in the one-band strip region
+    p = P(3, 8, 1 << 20, strip=256)
+    assert B.lce_workspace_bytes(p) == 256 + 16 * 256 * 2
 
 
 def test_pick_strip_policy(lib):

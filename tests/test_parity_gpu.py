@@ -238,7 +238,7 @@ def test_strip_width_policy():
     hid, wt, t = S.hidden(w), S.weight(w), S.targets(w)
     h, W, tt = to_gpu(w, hid, wt, t)
     p0 = B.make_problem(h, W, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, strip=0)
-    assert B.lce_workspace_bytes(p0) == 256 + 1000 * 5120 * 2
+    assert B.lce_workspace_bytes(p0) == 256 + 1008 * 5120 * 2
     vs = B.lce_pick_strip(p0, 1 << 20)
     assert vs == 512
     p1 = B.make_problem(h, W, ignore_index=S.IGNORE_INDEX, reduction=w.reduction, strip=vs)
@@ -419,7 +419,8 @@ def test_full_size_sampled(name):
         f"(workspace {ws_bytes / 1e9:.3f} GB, full logits {w.n_tokens * w.vocab * 2 / 1e9:.2f} GB)")
     assert peak_extra <= ws_bytes + outputs + (64 << 20)
     ldg = (w.strip + 255) // 256 * 256
-    assert ws_bytes == w.n_tokens * ldg * w.elt_bytes + 256  # one strip + control block
+    rows = (w.n_tokens + 15) // 16 * 16
+    assert ws_bytes == rows * ldg * w.elt_bytes + 256  # one strip + control block
 
     assert_loss(w, out["loss"], float(g["loss"]))
     assert_lse(out["lse"], g["lse"])

@@ -47,8 +47,8 @@ bool problem_ok(const lce_problem_t* p) {
 
 size_t elt_of(int dtype) { return dtype == LCE_BF16 ? 2 : 4; }
 
-// Workspace: a 256-byte control block, then one strip region of N x ldg
-// elements.  The backward keeps its gradient strip G there; the forward keeps
+// Workspace: a 256-byte control block, then one strip region of
+// round_up(N, 16) x ldg elements.  The backward keeps its gradient strip G there; the forward keeps
 // the running per-token state (max, sum, target logit; each column padded to
 // 256 bytes) at the region's end and its per-block partials [blocks, N] of
 // (max, sum) before it.  The region is the larger of the two needs; the
@@ -62,7 +62,8 @@ size_t partial_bytes(int64_t n, int64_t ldg) { return (size_t)n * (size_t)(ldg /
 
 size_t bytes_for_strip(int64_t n, int64_t vs, size_t elt) {
   const int64_t ldg = round_up(vs, kStripTile);
-  const size_t g = (size_t)n * (size_t)ldg * elt;                            // backward G strip
+  // backward G strip: whole 16-token bands (bf16 strips are kept in blocks of 16 rows)
+  const size_t g = (size_t)round_up(n, 16) * (size_t)ldg * elt;
   const size_t fwd = partial_bytes(n, ldg) + 3 * state_col_bytes(n);      // forward use
   return kHeader + (g > fwd ? g : fwd);
 }

@@ -29,6 +29,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// bf16 gradient strips are kept in blocks (BlockedG); f32 ones row-major
+// [N, ldg].
+template <typename T> constexpr bool kGBlocked = false;
+template <> constexpr bool kGBlocked<__bf16> = true;
+
 // ---------------------------------------------------------------------------
 // Forward strip: MFMA M = vocabulary rows of the strip, N = tokens, K = H.
 // ---------------------------------------------------------------------------
@@ -359,6 +364,105 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
   }
 }
 
+// bf16 strips in the strip buffer: G is kept in blocks (BlockedG, 16 tokens x
+// 32 vocabulary rows per kilobyte), so every wave stores its gradient values
+// straight from registers, one whole block per store instruction, with no LDS
+// staging and no barrier.  Per element one FMA, one exp2 and half a packed
+// bf16 conversion (the token's |scale| folded into the exponent, its sign
+// applied to the packed bits).  Two MFMA tiles mi = 2 p, 2 p + 1 of a column
+// block ni form block (token band, vocabulary column p) of the wave: lane
+// group g holds vocabulary rows 4 g .. + 3 of each; one permlane16 swap per
+// packed dword gives every lane 16 contiguous bytes of a block row (groups 0
+// and 2 the first tile's halves, groups 1 and 3 the second's).  Targets and
+// lse are loaded before any store.
+__device__ __forceinline__ void grad_epilogue_blocked(const StripArgs<__bf16>& a, Acc& acc,
+                                                      int64_t m0, int64_t n0) {
+  const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t vrow0 = m0 + wm * kWaveM;
+  const bool full = vrow0 + kWaveM <= a.v_len;
+  const int rows_left = full ? kWaveM : (int)max<int64_t>(a.v_len - vrow0, 0);
+  const int r_lane = (lane >> 4) * 4;
+  const float scale_all = a.ctrl->grad_scale;
+  const float abs_scale = fabsf(scale_all);
+  const uint32_t sign = scale_all < 0.f ? 0x80008000u : 0u;
+  const float log2_scale = __builtin_amdgcn_logf(abs_scale);
+
+  float c[kNI];
+  int tl[kNI];
+  bool any_hit[kNI];
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    const int64_t tok = n0 + wn * kWaveN + ni * kMfma + (lane & 15);
+    const bool tok_ok = tok < a.N;
+    const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
+    const bool valid = t != a.ignore_index;
+    const float lse2 = (tok_ok ? a.lse[tok] : 0.f) * kLog2e;
+    c[ni] = valid ? log2_scale - lse2 : -INFINITY;
+    const int64_t tl64 = (int64_t)t - (a.v_begin + vrow0);
+    const bool hit = valid && tl64 >= 0 && tl64 < kWaveM;
+    tl[ni] = hit ? (int)tl64 : -1;
+    any_hit[ni] = __any(hit);
+  }
+
+  // blocks from the tile's first one: band n0 / 16, block column m0 / 32;
+  // bands past the strip buffer's last (tokens past round_up(N, 16)) are
+  // out of range
+  const int64_t band = BlockedG::band_bytes(a.ldg, 2);
+  const int64_t col0 = (m0 / 32) * BlockedG::kBlkBytes;
+  const __amdgpu_buffer_rsrc_t gbuf =
+      make_buffer(reinterpret_cast<char*>(a.g_strip) + (n0 / 16) * band + col0,
+                  ((a.N + 15) / 16 - n0 / 16) * band - col0);
+  const int g = lane >> 4;
+  // byte offset of this lane's 16 bytes in the wave's first block (bands are
+  // below 2^26 bytes apart: ldg <= 2^21)
+  const uint32_t band32 = (uint32_t)band;
+  const uint32_t off0 = (uint32_t)(wn * (kWaveN / 16)) * band32 +
+                        (uint32_t)(wm * (kWaveM / 32) * BlockedG::kBlkBytes) +
+                        (uint32_t)((lane & 15) * BlockedG::kRowBytes + (((g & 1) << 1) | (g >> 1)) * 16);
+  // One 16-token column block at a time: its 32 values per lane, the row and
+  // target tests as wave-uniform branches over all of them (selects per
+  // element would triple the VALU work), then four packed block stores.
+#pragma unroll
+  for (int ni = 0; ni < kNI; ++ni) {
+    float v[4 * kMI];
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[mi * 4 + e] = fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, c[ni]));
+    if (!full) {
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[mi * 4 + e] = r_lane < rows_left - acc_row(mi, e, 0) ? v[mi * 4 + e] : 0.f;
+    }
+    if (any_hit[ni]) {
+      const int d = tl[ni] - r_lane;
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[mi * 4 + e] = d == acc_row(mi, e, 0) ? v[mi * 4 + e] - abs_scale : v[mi * 4 + e];
+    }
+#pragma unroll
+    for (int p = 0; p < kMI / 2; ++p) {
+      const u32x2_t q0 = GPack<__bf16>::pack(v[8 * p], v[8 * p + 1], v[8 * p + 2], v[8 * p + 3]);
+      const u32x2_t q1 =
+          GPack<__bf16>::pack(v[8 * p + 4], v[8 * p + 5], v[8 * p + 6], v[8 * p + 7]);
+      const auto x = __builtin_amdgcn_permlane16_swap(q0[0] ^ sign, q1[0] ^ sign, false, false);
+      const auto y = __builtin_amdgcn_permlane16_swap(q0[1] ^ sign, q1[1] ^ sign, false, false);
+      const u32x4_t val{x[0], y[0], x[1], y[1]};
+      const uint32_t off = off0 + (uint32_t)ni * band32 + (uint32_t)(p * BlockedG::kBlkBytes);
+      __builtin_amdgcn_raw_buffer_store_b128(val, gbuf, off, 0, 0);
+    }
+    sched_fence();  // one column block at a time: its 32 values, then the next
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -367,7 +471,10 @@ __global__ __launch_bounds__(kThreads, 1) void strip_grad_kernel(StripArgs<T> a)
   const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
   run_tiles<T, true, true>(A, B, a.H, grid, lds,
                            [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
-                             grad_epilogue(a, acc, m0, n0, staging, strip_dst(a, m0, n0));
+                             if constexpr (kGBlocked<T>)
+                               grad_epilogue_blocked(a, acc, m0, n0);
+                             else
+                               grad_epilogue(a, acc, m0, n0, staging, strip_dst(a, m0, n0));
                            });
 }
 
@@ -472,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g)
   const Operand<T> A{g.a, g.lda, g.a_mn_ext, g.a_k_ext};
   const Operand<T> B{g.b, g.ldb, g.b_mn_ext, g.b_k_ext};
   const TileGrid grid{g.m_tiles, g.n_tiles, g.group_m, blockIdx.x, gridDim.x, kGemmBands};
-  run_tiles<T, AK, BK>(A, B, g.k_len, grid, lds,
+  run_tiles<T, AK, BK, kGBlocked<T>>(A, B, g.k_len, grid, lds,
                        [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
                          gemm_epilogue<T, Accum>(g, acc, m0, n0, staging);
                        });
@@ -491,19 +598,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dh_dw_kernel(GemmArgs<T> dh,
     const Operand<T> A{dh.a, dh.lda, dh.a_mn_ext, dh.a_k_ext};
     const Operand<T> B{dh.b, dh.ldb, dh.b_mn_ext, dh.b_k_ext};
     const TileGrid grid{dh.m_tiles, dh.n_tiles, dh.group_m, b, split, kGemmBands};
-    run_tiles<T, true, false>(A, B, dh.k_len, grid, lds,
-                              [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
-                                gemm_epilogue<T, AccumDh>(dh, acc, m0, n0, staging);
-                              });
+    run_tiles<T, true, false, kGBlocked<T>>(A, B, dh.k_len, grid, lds,
+                                            [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
+                                              gemm_epilogue<T, AccumDh>(dh, acc, m0, n0, staging);
+                                            });
   } else {
     const Operand<T> A{dw.a, dw.lda, dw.a_mn_ext, dw.a_k_ext};
     const Operand<T> B{dw.b, dw.ldb, dw.b_mn_ext, dw.b_k_ext};
     const TileGrid grid{dw.m_tiles, dw.n_tiles, dw.group_m, b - split, gridDim.x - split,
                         kGemmBands};
-    run_tiles<T, false, false>(A, B, dw.k_len, grid, lds,
-                               [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
-                                 gemm_epilogue<T, AccumDw>(dw, acc, m0, n0, staging);
-                               });
+    run_tiles<T, false, false, kGBlocked<T>>(A, B, dw.k_len, grid, lds,
+                                             [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
+                                               gemm_epilogue<T, AccumDw>(dw, acc, m0, n0, staging);
+                                             });
   }
 }
 

@@ -31,10 +31,15 @@
 //    index swizzled by the k-row) and read with ds_read_b64_tr_b16, which
 //    hands each lane four K values of one column; two such reads make a
 //    fragment.  f32 stages (16 k-rows of 1 KiB) are read one float at a time.
-// The MN-contiguous swizzle and the split K-contiguous placement (below) keep
+// The MN-contiguous swizzles and the split K-contiguous placement (below) keep
 // every fragment read free of LDS bank conflicts (64 four-byte banks, 256
-// bytes per cycle); the row-major K-contiguous placement, kept beside a
-// transposed operand where it measured faster, costs a 2-way conflict.
+// bytes per cycle); the row-major K-contiguous placement, kept for the f32
+// gradient strip beside a transposed operand, costs a 2-way conflict.
+//
+// The bf16 gradient strip (the A operand of dH and dW) is kept in 1 KiB blocks
+// of 16 tokens x 64 bytes (BlockedG), so that a copy of either GEMM moves one
+// contiguous kilobyte and the gradient epilogue stores whole blocks from
+// registers.
 //
 // Loads go through buffer resources whose record count ends at the last
 // valid row, so rows past the operand's extent read as zeros and nothing is
@@ -151,8 +156,29 @@ struct Operand {
 // Operand layouts in LDS: MN-contiguous (the copy descriptor recomputed per
 // stage, or followed by adds), K-contiguous row-major, and K-contiguous with
 // the split sub-tile placement below.
-enum : int { kMN = 0, kKRow = 1, kKSplit = 2, kMNStep = 3 };
-__host__ __device__ constexpr bool is_mn(int l) { return l == kMN || l == kMNStep; }
+enum : int {
+  kMN = 0, kKRow = 1, kKSplit = 2, kMNStep = 3,
+  // a bf16 gradient strip kept in blocks (see BlockedG below): the split
+  // K-contiguous LDS layout, and a blocked transposed one
+  kKSplitBlk = 5, kMNBlkStep = 6
+};
+__host__ __device__ constexpr bool is_mn(int l) { return l == kMN || l == kMNStep || l == kMNBlkStep; }
+
+// A gradient strip in blocks: element (t, v) of an operand with row length ld
+// (elements) lives in block (t / 16, v / kBlkCols) of 16 rows x 64 bytes
+// (1 KiB), blocks of one 16-row band side by side along v, bands ld * elt * 16
+// bytes apart; inside a block the rows are 64 bytes apart.  A 64-byte K stage
+// of 16 rows - a K-contiguous copy, or the accumulators of two 16 x 16 MFMA
+// tiles of one wave - is then one contiguous kilobyte.
+struct BlockedG {
+  static constexpr int kBlkBytes = 1024;
+  static constexpr int kBlkRows = 16;
+  static constexpr int kRowBytes = 64;
+  // bytes between 16-row bands of an operand whose rows hold ld elements of elt bytes
+  __host__ __device__ static constexpr int64_t band_bytes(int64_t ld, int64_t elt) {
+    return ld * elt * kBlkRows;
+  }
+};
 template <typename T, int L> struct Side;
 
 // Buffer descriptor of an MN-contiguous operand's current stage (kElt-byte
@@ -200,7 +226,7 @@ struct MNDesc {
 // beside it (dH) the row-major one measured 3% faster.  Copy i of wave w
 // fills block c = c w + i (c = kCopiesPerWave): lane l reads physical chunk
 // l % kChunks of the row in slot l / kChunks, 64 contiguous bytes per 4 lanes.
-template <typename T, bool Split>
+template <typename T, bool Split, bool Blk = false>
 struct SideK {
   u32x4_t rsrc;
   uint32_t voff[kCopiesPerWave];
@@ -208,9 +234,15 @@ struct SideK {
   int64_t k_ext_bytes;
   uint32_t frag_off[2];  // byte offset of this lane's fragment, even and odd sub-tile of pair 0
 
-  // Point the copies at the tile whose first row is mn0.
+  // Point the copies at the tile whose first row is mn0 (a multiple of 16).
   __device__ __forceinline__ void retarget(const Operand<T>& op, int64_t mn0) {
-    rsrc = make_rsrc(op.base + mn0 * op.ld, (op.mn_ext - mn0) * op.ld * (int64_t)sizeof(T));
+    if constexpr (Blk) {
+      const int64_t band = BlockedG::band_bytes(op.ld, sizeof(T));
+      rsrc = make_rsrc(reinterpret_cast<const char*>(op.base) + (mn0 / 16) * band,
+                       ((op.mn_ext + 15) / 16 - mn0 / 16) * band);
+    } else {
+      rsrc = make_rsrc(op.base + mn0 * op.ld, (op.mn_ext - mn0) * op.ld * (int64_t)sizeof(T));
+    }
   }
   __device__ __forceinline__ void step() {}  // stages differ by the scalar offset only
   // Per-lane copy and fragment offsets (the same for every tile).
@@ -225,7 +257,11 @@ struct SideK {
       const int c = kCopiesPerWave * wave + i;  // block
       const int row = Split ? 32 * (c >> 1) + 16 * (slot >> 3) + 8 * (c & 1) + (slot & 7)
                             : 16 * c + slot;
-      voff[i] = (uint32_t)(row * row_bytes) + kbyte;
+      if constexpr (Blk)
+        voff[i] = (uint32_t)((row / 16) * BlockedG::band_bytes(op.ld, sizeof(T)) +
+                             (row % 16) * BlockedG::kRowBytes) + kbyte;
+      else
+        voff[i] = (uint32_t)(row * row_bytes) + kbyte;
     }
     // fragment: row j = lane % 16 of the sub-tile, logical chunk lane / 16
     // (K elements 8 (lane / 16) .. + 8 of bf16, 4 (lane / 16) .. + 4 of f32).
@@ -245,12 +281,13 @@ struct SideK {
     retarget(op, mn0);
   }
   // Copy stage kt (K bytes [kt, kt + 1) * kStageRowBytes) to LDS address dst;
-  // a dead copy (live == false) reads zeros.
+  // a dead copy (live == false) reads zeros.  In blocks, stage kt is block
+  // column kt of the band.
   // Copy i (< kCopiesPerWave) of this wave.
   __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
                                           int i) const {
     const int64_t k0 = kt * kStageRowBytes;
-    const uint32_t soff = live ? (uint32_t)k0 : 0u;
+    const uint32_t soff = live ? (uint32_t)(Blk ? kt * BlockedG::kBlkBytes : k0) : 0u;
     const bool ok = live && k0 + kbyte < k_ext_bytes;
     dma16(rsrc, dst + (kCopiesPerWave * wave + i) * 1024, ok ? voff[i] : kOutOfRange, soff);
   }
@@ -271,6 +308,7 @@ struct SideK {
 
 template <typename T> struct Side<T, kKRow> : SideK<T, false> {};
 template <typename T> struct Side<T, kKSplit> : SideK<T, true> {};
+template <> struct Side<__bf16, kKSplitBlk> : SideK<__bf16, true, true> {};
 
 // MN-contiguous bf16 operand: a stage is kStageRowBytes / 2 k-rows x 256 mn.
 // Copy i of wave w covers k-rows 2 (c w + i) and +1 (c = kCopiesPerWave); lane
@@ -334,6 +372,87 @@ struct SideMNb16 {
   }
 };
 
+// MN-contiguous bf16 operand kept in blocks (BlockedG: k-rows are the 16-row
+// bands' rows, mn runs along a band).  A stage (32 k-rows = two bands, 256 mn
+// = eight block columns) is kept in LDS as the same 16 blocks of 1 KiB, block
+// (column cb, band b) at (2 cb + b) KiB, so every copy moves one whole block
+// (1 KiB contiguous in memory).  Inside a block, row r's 16-byte chunk c sits
+// at chunk c ^ (2 (r >> 3 & 1)): a transposed fragment read takes 32 bytes of
+// each of the rows {0..3, 8..11} of a band per 32 lanes (+ 4 for its second
+// read), and rows r and r + 8 of one 64-byte window then land on opposite
+// halves of it, which keeps the reads free of bank conflicts.  The descriptor
+// follows the stages by adds.
+struct SideMNb16Blk {
+  const char* base;  // stage's first band, at the tile's first block column
+  int64_t bytes;     // from base to the operand's last band's end
+  int64_t band;      // bytes between bands
+  uint32_t voff[kCopiesPerWave];
+  uint32_t frag_off[kMI];
+
+  __device__ __forceinline__ static int chunk_swz(int r) { return ((r >> 3) & 1) << 1; }
+
+  __device__ __forceinline__ void retarget(const Operand<__bf16>& op, int64_t mn0) {
+    band = BlockedG::band_bytes(op.ld, 2);
+    const int64_t col = (mn0 / 32) * BlockedG::kBlkBytes;  // mn0 is a multiple of 256
+    base = reinterpret_cast<const char*>(op.base) + col;
+    bytes = ((op.k_ext + 15) / 16) * band - col;
+  }
+  __device__ __forceinline__ void step() {
+    base += 2 * band;
+    bytes -= 2 * band;
+  }
+  __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane,
+                                       int sub0) {
+    init_lanes(op, wave, lane, sub0);
+    retarget(op, mn0);
+  }
+  __device__ __forceinline__ void init_lanes(const Operand<__bf16>& op, int wave, int lane,
+                                             int sub0) {
+    const int64_t bb = BlockedG::band_bytes(op.ld, 2);
+    // lane l fills LDS slot l of its copy's block: row l / 4, physical chunk
+    // l % 4, i.e. the block's logical chunk (l % 4) ^ chunk_swz(row)
+    const int r = lane >> 2;
+    const int lchunk = (lane & 3) ^ chunk_swz(r);
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+      const int bi = kCopiesPerWave * wave + i;  // LDS block: column bi / 2, band bi % 2
+      voff[i] = (uint32_t)((bi & 1) * bb + (bi >> 1) * BlockedG::kBlkBytes +
+                           r * BlockedG::kRowBytes + lchunk * 16);
+    }
+    // ds_read_b64_tr_b16: lane jj of group g addresses k-row 8 g + jj / 4 (and
+    // + 4 for the second read) and the 4 columns 4 (jj % 4) of the sub-tile
+    const int g = lane >> 4, jj = lane & 15;
+    const int kr = 8 * g + (jj >> 2);
+    const int rb = kr & 15, bnd = kr >> 4;
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi) {
+      const int col = sub0 + mi * kMfma + 4 * (jj & 3);
+      const int cb = col >> 5, cc = col & 31;
+      frag_off[mi] = (uint32_t)((2 * cb + bnd) * BlockedG::kBlkBytes + rb * BlockedG::kRowBytes +
+                                (((cc >> 3) ^ chunk_swz(rb)) * 16) + (cc & 7) * 2);
+    }
+  }
+  __device__ __forceinline__ void copy_one(uint32_t dst, int64_t, int wave, bool live,
+                                          int i) const {
+    dma16(make_rsrc(base, bytes), dst + (kCopiesPerWave * wave + i) * 1024,
+          live ? voff[i] : kOutOfRange, 0);
+  }
+  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
+#pragma unroll
+    for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
+  }
+  // The second read is 4 k-rows further: 4 block rows, the same swizzle.
+  __device__ __forceinline__ u32x4_t frag(const char* src, int mi) const {
+    const char* p = src + frag_off[mi];
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(p + 4 * BlockedG::kRowBytes));
+    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo);
+    const u32x2_t h2 = __builtin_bit_cast(u32x2_t, hi);
+    return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+  }
+};
+
 // MN-contiguous f32 operand: a stage is kStageRowBytes / 4 k-rows of 256
 // floats (1 KiB), one k-row per copy, no swizzle; fragments are read one float
 // at a time.
@@ -386,6 +505,7 @@ template <> struct Side<__bf16, kMN> : SideMNb16<false> {};
 template <> struct Side<__bf16, kMNStep> : SideMNb16<true> {};
 template <> struct Side<float, kMN> : SideMNf32<false> {};
 template <> struct Side<float, kMNStep> : SideMNf32<true> {};
+template <> struct Side<__bf16, kMNBlkStep> : SideMNb16Blk {};
 
 // ---------------------------------------------------------------------------
 // MFMA on one 16-byte fragment pair.
@@ -635,7 +755,8 @@ __device__ __forceinline__ void half_stage(const Side<T, AK>& sa, const Side<T, 
 // cannot be counted in n.  The first wait after an epilogue (half a stage
 // into the next tile) therefore also waits for the epilogue's stores to be
 // acknowledged.
-template <typename T, bool AK, bool BK, typename Epi>
+// ABlk: A is a bf16 gradient strip kept in blocks (BlockedG).
+template <typename T, bool AK, bool BK, bool ABlk = false, typename Epi>
 __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>& B, int64_t k_len,
                                           const TileGrid& grid, char* lds, Epi&& epi) {
   constexpr int64_t kStageK = kStageRowBytes / sizeof(T);
@@ -660,7 +781,13 @@ __device__ __forceinline__ void run_tiles(const Operand<T>& A, const Operand<T>&
   // K-contiguous operands take the split placement when both are (strip
   // kernels), the row-major one beside a transposed operand.
   // MN-contiguous descriptors follow by adds where both operands are (dW).
-  constexpr int LA = !AK ? (BK ? kMN : kMNStep) : (BK ? kKSplit : kKRow);
+  // A gradient strip in blocks (ABlk) takes the split placement (conflict-free
+  // fragment reads) when K-contiguous, the blocked transposed stage otherwise;
+  // with blocks, a split copy still reads two 512-byte runs, and measured
+  // faster than the row-major placement beside dH's transposed W (0.6% per
+  // step, same box).
+  constexpr int LA0 = !AK ? (BK ? kMN : kMNStep) : (BK ? kKSplit : kKRow);
+  constexpr int LA = !ABlk ? LA0 : (AK ? kKSplitBlk : kMNBlkStep);
   constexpr int LB = !BK ? (AK ? kMN : kMNStep) : (AK ? kKSplit : kKRow);
   Cursor<T, LA> ca{{}, 0, 0, 0u};
   Cursor<T, LB> cb{{}, 0, 0, 0u};
