@@ -208,7 +208,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-KERNEL_SOURCES = ("tile_engine.h", "lce_kernels.hip", "lce_kernels.h")
+KERNEL_SOURCES = ("tile_engine.h", "tile_engine_w4.h", "lce_kernels.hip", "lce_kernels.h")
 
 
 def kernel_source_sha256() -> str:
@@ -248,7 +248,8 @@ def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, 
     the backward runs strip_grad, then dH and dW as two launches or as the one
     shared launch that lce_backward_fold makes for that strip."""
     kernels = {
-        "strip_lse": "lce::strip_lse_kernel",
+        "strip_lse": ("lce::strip_lse_kernel_w4" if w.dtype == "bf16"
+                      else "lce::strip_lse_kernel<float>"),
         "merge": "lce::fold_kernel",
         "strip_grad": "lce::strip_grad_kernel",
         "gemm_dh": "lce::gemm_f32out_kernel<A K-contig, B MN-contig>",

@@ -158,6 +158,15 @@ SMALL = [
     # few tokens, a vocabulary past 2^18: the forward's folds of up to
     # 261888 rows split it in two (261888 + 38112)
     S.small("bf16_small_n_huge_v", 300, 64, 300000, 8192, ignore_frac=0.1),
+    # the one-wave-per-SIMD strip kernels (bf16 with H >= 1024): a K tail of
+    # 8 elements in the 17th stage, ragged tokens and vocabulary
+    S.small("bf16_w4_ragged", 1000, 1032, 3001, 1024, ignore_frac=0.1),
+    # several tiles per persistent block, so the copy stream crosses tile
+    # boundaries (strips of 17 x 32 and 17 x 15 tiles, a forward of 17 x 47)
+    S.small("bf16_w4_multi_tile", 4100, 1024, 12000, 8192, reduction="sum", grad_out=0.37,
+            target_law="zipf", ignore_frac=0.05),
+    # a vocabulary tail of 40 rows, 5 tokens in the last band of 16
+    S.small("bf16_w4_short_tails", 517, 1088, 552, 512, ignore_frac=0.1),
 ]
 
 

@@ -19,9 +19,11 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "lce_kernels.h"
 #include "tile_engine.h"
+#include "tile_engine_w4.h"
 
 namespace lce {
 
@@ -41,9 +43,10 @@ template <> constexpr bool kGBlocked<__bf16> = true;
 // exp(z - max)) to partials, and the target logit to z_target.  A token's
 // 128 rows of a wave sit in the four lanes l % 16 + 16 h (h = 0..3), 32
 // values each.
-template <typename T>
-__device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, Acc& acc, int64_t m0,
+template <typename T, typename AccT>
+__device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, AccT& acc, int64_t m0,
                                              int64_t n0) {
+  constexpr int kMI = AccT::MI, kNI = AccT::NI, kWaveM = AccT::WaveM, kWaveN = AccT::WaveN;
   // lane values recomputed per tile rather than hoisted and kept live
   const int tid = opaque((int)threadIdx.x);
   const int lane = tid & 63;
@@ -67,7 +70,7 @@ __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, Acc& acc, in
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[mi * 4 + e] = acc.c[mi][ni][e];
+      for (int e = 0; e < 4; ++e) v[mi * 4 + e] = AccT::read(acc.c[mi][ni], e);
     if (!full) {
       // rows past the strip's end: -inf adds nothing to the max or the sum
 #pragma unroll
@@ -109,6 +112,18 @@ __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, Acc& acc, in
     }
     sched_fence();
   }
+}
+
+// The forward strip on the one-wave-per-SIMD engine (bf16).
+__global__ __launch_bounds__(w4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void strip_lse_kernel_w4(StripArgs<__bf16> a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const Operand<__bf16> A{a.weight_strip, a.H, a.v_len, a.H};
+  const Operand<__bf16> B{a.hidden, a.H, a.N, a.H};
+  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
+  w4::run_tiles(A, B, a.H, grid, lds, [&](w4::Acc& acc, int64_t m0, int64_t n0) {
+    lse_epilogue(a, acc, m0, n0);
+  });
 }
 
 template <typename T>
@@ -375,8 +390,10 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
 // packed dword gives every lane 16 contiguous bytes of a block row (groups 0
 // and 2 the first tile's halves, groups 1 and 3 the second's).  Targets and
 // lse are loaded before any store.
-__device__ __forceinline__ void grad_epilogue_blocked(const StripArgs<__bf16>& a, Acc& acc,
+template <typename AccT>
+__device__ __forceinline__ void grad_epilogue_blocked(const StripArgs<__bf16>& a, AccT& acc,
                                                       int64_t m0, int64_t n0) {
+  constexpr int kMI = AccT::MI, kNI = AccT::NI, kWaveM = AccT::WaveM, kWaveN = AccT::WaveN;
   const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -432,7 +449,7 @@ __device__ __forceinline__ void grad_epilogue_blocked(const StripArgs<__bf16>& a
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        v[mi * 4 + e] = fast_exp2(__builtin_fmaf(acc.c[mi][ni][e], kLog2e, c[ni]));
+        v[mi * 4 + e] = fast_exp2(__builtin_fmaf(AccT::read(acc.c[mi][ni], e), kLog2e, c[ni]));
     if (!full) {
 #pragma unroll
       for (int mi = 0; mi < kMI; ++mi)
@@ -461,6 +478,18 @@ __device__ __forceinline__ void grad_epilogue_blocked(const StripArgs<__bf16>& a
     }
     sched_fence();  // one column block at a time: its 32 values, then the next
   }
+}
+
+// The backward strip on the one-wave-per-SIMD engine (bf16, blocked G).
+__global__ __launch_bounds__(w4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void strip_grad_kernel_w4(StripArgs<__bf16> a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const Operand<__bf16> A{a.weight_strip, a.H, a.v_len, a.H};
+  const Operand<__bf16> B{a.hidden, a.H, a.N, a.H};
+  const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
+  w4::run_tiles(A, B, a.H, grid, lds, [&](w4::Acc& acc, int64_t m0, int64_t n0) {
+    grad_epilogue_blocked(a, acc, m0, n0);
+  });
 }
 
 template <typename T>
@@ -956,11 +985,45 @@ static int64_t stages_of(int64_t k_len) {
   return (k_len + kStageK - 1) / kStageK;
 }
 
+// A strip kernel on the one-wave-per-SIMD engine, in persistent blocks (its
+// copy stream needs at least two K stages per tile).
+static hipError_t launch_w4(void (*kernel)(StripArgs<__bf16>), const StripArgs<__bf16>& a,
+                            hipStream_t st) {
+  if (cdiv(a.H, w4::kStageK) < 2) return hipErrorInvalidValue;
+  const int64_t tiles = a.m_tiles * a.n_tiles;
+  const int64_t p = persistent_blocks();
+  const int64_t blocks = tiles < p ? tiles : p;
+  if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, w4::kLdsBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(w4::kThreads), w4::kLdsBytes, st, a);
+  return hipGetLastError();
+}
+
+// bf16 strips of at least 16 K stages (H >= 1024) run on the one-wave-per-SIMD
+// engine; shorter ones, and fp32, on the eight-wave engine.  With a single
+// wave on a SIMD nothing covers a tile's epilogue, which the MFMAs of 16
+// stages amortise and those of 8 do not: at H = 512 the one-wave forward took
+// 11% longer than the eight-wave one, at H = 2048 it was 1.5% slower at 4096
+// tokens and 4% faster at 131072, at H = 6144 5% faster.
+constexpr int64_t kW4MinStages = 16;
+
+template <typename T>
+static bool use_w4(const StripArgs<T>& a) {
+  if constexpr (std::is_same<T, __bf16>::value)
+    return cdiv(a.H, w4::kStageK) >= kW4MinStages;
+  else
+    return false;
+}
+
 template <typename T>
 hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st) {
   a.m_tiles = cdiv(a.v_len, kTile);
   a.n_tiles = cdiv(a.N, kTile);
   a.group_m = kStripGroupM;
+  if constexpr (std::is_same<T, __bf16>::value)
+    if (use_w4(a)) return launch_w4(strip_lse_kernel_w4, a, st);
   const int64_t blocks = grid_blocks(a.m_tiles * a.n_tiles, stages_of<T>(a.H));
   if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_lse_kernel<T>));
@@ -974,6 +1037,8 @@ hipError_t launch_strip_grad(StripArgs<T> a, hipStream_t st) {
   a.m_tiles = cdiv(a.v_len, kTile);
   a.n_tiles = cdiv(a.N, kTile);
   a.group_m = kStripGroupM;
+  if constexpr (std::is_same<T, __bf16>::value)
+    if (use_w4(a)) return launch_w4(strip_grad_kernel_w4, a, st);
   const int64_t blocks = grid_blocks(a.m_tiles * a.n_tiles, stages_of<T>(a.H));
   if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_grad_kernel<T>));

@@ -544,7 +544,9 @@ struct Mfma<float> {
 // Element (mi, ni, e) of lane l sits at tile row
 //   wm*kWaveM + mi*16 + (l/16)*4 + e   and column  wn*kWaveN + ni*16 + l%16.
 struct Acc {
+  static constexpr int MI = kMI, NI = kNI, WaveM = kWaveM, WaveN = kWaveN;
   f32x4_t c[kMI][kNI];
+  __device__ __forceinline__ static float read(const f32x4_t& v, int e) { return v[e]; }
 };
 
 __device__ __forceinline__ int acc_row(int mi, int e, int lane) {
