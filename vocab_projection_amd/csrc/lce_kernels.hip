@@ -121,9 +121,10 @@ void strip_lse_kernel_w4(StripArgs<__bf16> a) {
   const Operand<__bf16> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<__bf16> B{a.hidden, a.H, a.N, a.H};
   const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
-  w4::run_tiles(A, B, a.H, grid, lds, [&](w4::Acc& acc, int64_t m0, int64_t n0) {
-    lse_epilogue(a, acc, m0, n0);
-  });
+  w4::run_tiles<w4::KRow128, w4::KRow128>(A, B, a.H, grid, lds,
+                                          [&](w4::Acc& acc, int64_t m0, int64_t n0, char*) {
+                                            lse_epilogue(a, acc, m0, n0);
+                                          });
 }
 
 template <typename T>
@@ -487,9 +488,10 @@ void strip_grad_kernel_w4(StripArgs<__bf16> a) {
   const Operand<__bf16> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<__bf16> B{a.hidden, a.H, a.N, a.H};
   const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
-  w4::run_tiles(A, B, a.H, grid, lds, [&](w4::Acc& acc, int64_t m0, int64_t n0) {
-    grad_epilogue_blocked(a, acc, m0, n0);
-  });
+  w4::run_tiles<w4::KRow128, w4::KRow128>(A, B, a.H, grid, lds,
+                                          [&](w4::Acc& acc, int64_t m0, int64_t n0, char*) {
+                                            grad_epilogue_blocked(a, acc, m0, n0);
+                                          });
 }
 
 template <typename T>
@@ -612,6 +614,121 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f32out_kernel(GemmArgs<T> g)
                        [&](Acc& acc, int64_t m0, int64_t n0, char* staging) {
                          gemm_epilogue<T, Accum>(g, acc, m0, n0, staging);
                        });
+}
+
+// The fp32-output epilogue of the one-wave-per-SIMD engine: rows of C move
+// through the kStagingBytes after its stage buffers in eight passes of 32
+// rows, pass p taking the 16 rows of MFMA sub-tile p from each half of the
+// tile (tile rows 16 p .. 16 p + 15 and 128 + 16 p ..), so that every wave
+// writes its share of every pass; then all four waves move whole rows, 1 KiB
+// of C per instruction.  Staging row r holds tile row (r / 16) 128 + 16 p +
+// r % 16.
+constexpr int kEpi4Rows = w4::kStagingBytes / kEpiRowBytes;  // 32
+
+template <typename T, bool Accum>
+__device__ __forceinline__ void gemm_epilogue_w4(const GemmArgs<T>& g, w4::Acc& acc, int64_t m0,
+                                                 int64_t n0, char* lds) {
+  const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t ldc4 = (uint32_t)(g.ldc * 4);
+  const __amdgpu_buffer_rsrc_t cbuf =
+      make_buffer(g.c + m0 * g.ldc + n0, (g.m - m0) * g.ldc * 4 - n0 * 4);
+  const int run = tid & 63;
+  const bool run_ok = n0 + 4 * run < g.n;
+  constexpr int kRowsPerThread = kEpi4Rows / w4::kWaves;  // 8: staging rows wave + 4 i
+  static_assert(kEpi4Rows == 2 * kMfma && w4::kMI * kMfma == w4::kWaveM, "pass geometry");
+
+#pragma unroll
+  for (int pass = 0; pass < w4::kMI; ++pass) {
+    // staging row wave + 4 i is tile row (i / 4) 128 + 16 pass + wave + 4 (i % 4)
+    auto row_off = [&](int i) -> uint32_t {
+      const int row = (i / 4) * w4::kWaveM + kMfma * pass + wave + 4 * (i % 4);
+      return run_ok ? (uint32_t)row * ldc4 + run * 16 : kOutOfRange;
+    };
+    constexpr int kEarly = kRowsPerThread / 2;
+    u32x4_t old[kRowsPerThread];
+    if constexpr (Accum) {
+#pragma unroll
+      for (int i = 0; i < kEarly; ++i)
+        old[i] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, row_off(i), 0, 0);
+    }
+    block_barrier();  // staging free: the previous pass (or tile) is done with it
+#pragma unroll
+    for (int ni = 0; ni < w4::kNI; ++ni) {
+      const int col = wn * w4::kWaveN + ni * kMfma + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = wm * kMfma + acc_row(0, e, lane);
+        *reinterpret_cast<float*>(lds + epi_offset(row, col >> 2) + (col & 3) * 4) =
+            w4::Acc::read(acc.c[pass][ni], e);
+      }
+    }
+    block_barrier();
+    f32x4_t v[kRowsPerThread];
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int row = wave + w4::kWaves * i;
+      v[i] = *reinterpret_cast<const f32x4_t*>(lds + epi_offset(row, run));
+    }
+    if constexpr (Accum) {
+#pragma unroll
+      for (int i = kEarly; i < kRowsPerThread; ++i)
+        old[i] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, row_off(i), 0, 0);
+#pragma unroll
+      for (int i = 0; i < kRowsPerThread; ++i) v[i] += __builtin_bit_cast(f32x4_t, old[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v[i]), cbuf, row_off(i),
+                                             0, 0);
+    sched_fence();
+  }
+}
+
+// dW (blocked G and h, both MN-contiguous) on the one-wave-per-SIMD engine;
+// AK = true is dH (K-contiguous blocked G, MN-contiguous W_s), which only the
+// shared launch below runs on it.
+template <bool AK, bool Accum>
+__global__ __launch_bounds__(w4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_f32out_kernel_w4(GemmArgs<__bf16> g) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const Operand<__bf16> A{g.a, g.lda, g.a_mn_ext, g.a_k_ext};
+  const Operand<__bf16> B{g.b, g.ldb, g.b_mn_ext, g.b_k_ext};
+  const TileGrid grid{g.m_tiles, g.n_tiles, g.group_m, blockIdx.x, gridDim.x, kGemmBands};
+  using SA = typename std::conditional<AK, w4::KSplitBlk, w4::MNBlk>::type;
+  w4::run_tiles<SA, w4::MN>(A, B, g.k_len, grid, lds,
+                            [&](w4::Acc& acc, int64_t m0, int64_t n0, char* staging) {
+                              gemm_epilogue_w4<__bf16, Accum>(g, acc, m0, n0, staging);
+                            });
+}
+
+// dH and dW sharing one launch (see gemm_dh_dw_kernel below) on the
+// one-wave-per-SIMD engine.
+template <bool AccumDh, bool AccumDw>
+__global__ __launch_bounds__(w4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_dh_dw_kernel_w4(GemmArgs<__bf16> dh, GemmArgs<__bf16> dw, int64_t split) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int64_t b = blockIdx.x;
+  if (b < split) {
+    const Operand<__bf16> A{dh.a, dh.lda, dh.a_mn_ext, dh.a_k_ext};
+    const Operand<__bf16> B{dh.b, dh.ldb, dh.b_mn_ext, dh.b_k_ext};
+    const TileGrid grid{dh.m_tiles, dh.n_tiles, dh.group_m, b, split, kGemmBands};
+    w4::run_tiles<w4::KSplitBlk, w4::MN>(
+        A, B, dh.k_len, grid, lds, [&](w4::Acc& acc, int64_t m0, int64_t n0, char* staging) {
+          gemm_epilogue_w4<__bf16, AccumDh>(dh, acc, m0, n0, staging);
+        });
+  } else {
+    const Operand<__bf16> A{dw.a, dw.lda, dw.a_mn_ext, dw.a_k_ext};
+    const Operand<__bf16> B{dw.b, dw.ldb, dw.b_mn_ext, dw.b_k_ext};
+    const TileGrid grid{dw.m_tiles, dw.n_tiles, dw.group_m, b - split, gridDim.x - split,
+                        kGemmBands};
+    w4::run_tiles<w4::MNBlk, w4::MN>(
+        A, B, dw.k_len, grid, lds, [&](w4::Acc& acc, int64_t m0, int64_t n0, char* staging) {
+          gemm_epilogue_w4<__bf16, AccumDw>(dw, acc, m0, n0, staging);
+        });
+  }
 }
 
 // dH and dW of one strip in one launch: blocks [0, split) form dH
@@ -1052,6 +1169,26 @@ static hipError_t launch_gemm(GemmArgs<T> g, hipStream_t st) {
   g.m_tiles = cdiv(g.m, kTile);
   g.n_tiles = cdiv(g.n, kTile);
   g.group_m = kGemmGroupM;
+  if constexpr (std::is_same<T, __bf16>::value && !AK && !BK) {
+    // dW on the one-wave-per-SIMD engine from 16 K stages on (5-6% faster at
+    // 131072 tokens).  dH stays on the eight-wave engine: on the one-wave
+    // engine its main loop was faster but the read-modify-write epilogue,
+    // which every compute unit reaches at once and nothing overlaps, made it
+    // 0.7-1.1% slower in three same-box comparisons.
+    if (cdiv(g.k_len, w4::kStageK) >= kW4MinStages) {
+      const int64_t tiles = g.m_tiles * g.n_tiles;
+      const int64_t p = persistent_blocks();
+      const int64_t blocks = tiles < p ? tiles : p;
+      if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
+      constexpr int kLds = w4::kLdsBytes + w4::kStagingBytes;
+      const void* k = reinterpret_cast<const void*>(&gemm_f32out_kernel_w4<AK, Accum>);
+      hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((gemm_f32out_kernel_w4<AK, Accum>), dim3((unsigned)blocks),
+                         dim3(w4::kThreads), kLds, st, g);
+      return hipGetLastError();
+    }
+  }
   const int64_t blocks = grid_blocks(g.m_tiles * g.n_tiles, stages_of<T>(g.k_len));
   if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
   hipError_t e =
@@ -1112,6 +1249,19 @@ hipError_t launch_dw(const T* g_strip, int64_t ldg, const T* hidden, int64_t v_l
 template <typename T, bool AccumDh, bool AccumDw>
 static hipError_t launch_dh_dw_shared(const GemmArgs<T>& dh, const GemmArgs<T>& dw, int64_t split,
                                       int64_t blocks, hipStream_t st) {
+  if constexpr (std::is_same<T, __bf16>::value) {
+    // on the one-wave-per-SIMD engine when both GEMMs have 16 K stages or more
+    if (cdiv(dh.k_len, w4::kStageK) >= kW4MinStages &&
+        cdiv(dw.k_len, w4::kStageK) >= kW4MinStages) {
+      constexpr int kLds = w4::kLdsBytes + w4::kStagingBytes;
+      const void* k = reinterpret_cast<const void*>(&gemm_dh_dw_kernel_w4<AccumDh, AccumDw>);
+      hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((gemm_dh_dw_kernel_w4<AccumDh, AccumDw>), dim3((unsigned)blocks),
+                         dim3(w4::kThreads), kLds, st, dh, dw, split);
+      return hipGetLastError();
+    }
+  }
   hipError_t e =
       set_lds<T>(reinterpret_cast<const void*>(&gemm_dh_dw_kernel<T, AccumDh, AccumDw>));
   if (e != hipSuccess) return e;

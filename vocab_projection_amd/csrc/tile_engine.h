@@ -133,8 +133,13 @@ __device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t lds, uint32_t voff,
                :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
+// Barrier of the block that also publishes this wave's LDS accesses: the
+// hardware barrier does not wait for them, so LDS writes (and reads) still in
+// flight are waited for first (lgkmcnt(0)); without it a wave past the barrier
+// could read staging rows before another wave's writes had landed.
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -224,12 +229,13 @@ struct MNDesc {
 // every read.  The split placement pays where both operands are
 // K-contiguous (the strip kernels, 1% faster); with a transposed operand
 // beside it (dH) the row-major one measured 3% faster.  Copy i of wave w
-// fills block c = c w + i (c = kCopiesPerWave): lane l reads physical chunk
+// fills block c = c w + i (c = CPW): lane l reads physical chunk
 // l % kChunks of the row in slot l / kChunks, 64 contiguous bytes per 4 lanes.
-template <typename T, bool Split, bool Blk = false>
+// CPW is the number of copies per wave (16 / waves per block).
+template <typename T, bool Split, bool Blk = false, int CPW = kCopiesPerWave>
 struct SideK {
   u32x4_t rsrc;
-  uint32_t voff[kCopiesPerWave];
+  uint32_t voff[CPW];
   uint32_t kbyte;        // byte column of this lane's logical chunk
   int64_t k_ext_bytes;
   uint32_t frag_off[2];  // byte offset of this lane's fragment, even and odd sub-tile of pair 0
@@ -253,8 +259,8 @@ struct SideK {
     static_assert(kRowsPerCopy == 16, "a copy fills one block of 16 slots");
     kbyte = (uint32_t)(((lane % kChunks) ^ swz_k(slot)) * 16);
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) {
-      const int c = kCopiesPerWave * wave + i;  // block
+    for (int i = 0; i < CPW; ++i) {
+      const int c = CPW * wave + i;  // block
       const int row = Split ? 32 * (c >> 1) + 16 * (slot >> 3) + 8 * (c & 1) + (slot & 7)
                             : 16 * c + slot;
       if constexpr (Blk)
@@ -283,17 +289,22 @@ struct SideK {
   // Copy stage kt (K bytes [kt, kt + 1) * kStageRowBytes) to LDS address dst;
   // a dead copy (live == false) reads zeros.  In blocks, stage kt is block
   // column kt of the band.
-  // Copy i (< kCopiesPerWave) of this wave.
+  // Copy i (< CPW) of this wave.
   __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
                                           int i) const {
     const int64_t k0 = kt * kStageRowBytes;
     const uint32_t soff = live ? (uint32_t)(Blk ? kt * BlockedG::kBlkBytes : k0) : 0u;
     const bool ok = live && k0 + kbyte < k_ext_bytes;
-    dma16(rsrc, dst + (kCopiesPerWave * wave + i) * 1024, ok ? voff[i] : kOutOfRange, soff);
+    dma16(rsrc, dst + (CPW * wave + i) * 1024, ok ? voff[i] : kOutOfRange, soff);
   }
   __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
+    for (int i = 0; i < CPW; ++i) copy_one(dst, kt, wave, live, i);
+  }
+  // The same, for a caller that never steps the side (stages differ only by kt).
+  __device__ __forceinline__ void copy_at(uint32_t dst, int64_t kt, int wave, bool live,
+                                         int i) const {
+    copy_one(dst, kt, wave, live, i);
   }
   // Fragment of 16-row sub-tile mi of the stage at src (pair mi / 2 is the
   // 32-row group's 2 KiB).
@@ -311,12 +322,12 @@ template <typename T> struct Side<T, kKSplit> : SideK<T, true> {};
 template <> struct Side<__bf16, kKSplitBlk> : SideK<__bf16, true, true> {};
 
 // MN-contiguous bf16 operand: a stage is kStageRowBytes / 2 k-rows x 256 mn.
-// Copy i of wave w covers k-rows 2 (c w + i) and +1 (c = kCopiesPerWave); lane
-// l fills physical chunk l % 32 of k-row 2 (c w + i) + l / 32.
-template <bool Step>
+// Copy i of wave w covers k-rows 2 (c w + i) and +1 (c = CPW, copies per
+// wave); lane l fills physical chunk l % 32 of k-row 2 (c w + i) + l / 32.
+template <bool Step, int CPW = kCopiesPerWave>
 struct SideMNb16 {
   MNDesc<Step, 2> d;
-  uint32_t voff[kCopiesPerWave];
+  uint32_t voff[CPW];
   uint32_t frag_off[kMI];  // per mi: byte offset of this lane's first transposed read
 
   __device__ __forceinline__ void retarget(const Operand<__bf16>& op, int64_t mn0) {
@@ -333,8 +344,8 @@ struct SideMNb16 {
     const int64_t row_bytes = op.ld * 2;
     d.row_bytes = row_bytes;
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) {
-      const int kr = 2 * (kCopiesPerWave * wave + i) + (lane >> 5);
+    for (int i = 0; i < CPW; ++i) {
+      const int kr = 2 * (CPW * wave + i) + (lane >> 5);
       const int c = (lane & 31) ^ swz_mn(kr);
       voff[i] = (uint32_t)(kr * row_bytes + c * 16);
     }
@@ -356,11 +367,16 @@ struct SideMNb16 {
   }
   __device__ __forceinline__ void copy_one(uint32_t dst, int64_t kt, int wave, bool live,
                                           int i) const {
-    dma16(d.rsrc(kt), dst + (kCopiesPerWave * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
+    dma16(d.rsrc(kt), dst + (CPW * wave + i) * 1024, live ? voff[i] : kOutOfRange, 0);
   }
   __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
+    for (int i = 0; i < CPW; ++i) copy_one(dst, kt, wave, live, i);
+  }
+  __device__ __forceinline__ void copy_at(uint32_t dst, int64_t kt, int wave, bool live,
+                                         int i) const {
+    static_assert(!Step, "a stepped descriptor depends on the stages copied before");
+    copy_one(dst, kt, wave, live, i);
   }
   __device__ __forceinline__ u32x4_t frag(const char* src, int mi) const {
     const char* p = src + frag_off[mi];
@@ -381,12 +397,14 @@ struct SideMNb16 {
 // each of the rows {0..3, 8..11} of a band per 32 lanes (+ 4 for its second
 // read), and rows r and r + 8 of one 64-byte window then land on opposite
 // halves of it, which keeps the reads free of bank conflicts.  The descriptor
-// follows the stages by adds.
+// follows the stages by adds (copy_one), or is computed from the stage
+// (copy_at, with the side never stepped).
+template <int CPW = kCopiesPerWave>
 struct SideMNb16Blk {
   const char* base;  // stage's first band, at the tile's first block column
   int64_t bytes;     // from base to the operand's last band's end
   int64_t band;      // bytes between bands
-  uint32_t voff[kCopiesPerWave];
+  uint32_t voff[CPW];
   uint32_t frag_off[kMI];
 
   __device__ __forceinline__ static int chunk_swz(int r) { return ((r >> 3) & 1) << 1; }
@@ -414,8 +432,8 @@ struct SideMNb16Blk {
     const int r = lane >> 2;
     const int lchunk = (lane & 3) ^ chunk_swz(r);
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) {
-      const int bi = kCopiesPerWave * wave + i;  // LDS block: column bi / 2, band bi % 2
+    for (int i = 0; i < CPW; ++i) {
+      const int bi = CPW * wave + i;  // LDS block: column bi / 2, band bi % 2
       voff[i] = (uint32_t)((bi & 1) * bb + (bi >> 1) * BlockedG::kBlkBytes +
                            r * BlockedG::kRowBytes + lchunk * 16);
     }
@@ -434,12 +452,19 @@ struct SideMNb16Blk {
   }
   __device__ __forceinline__ void copy_one(uint32_t dst, int64_t, int wave, bool live,
                                           int i) const {
-    dma16(make_rsrc(base, bytes), dst + (kCopiesPerWave * wave + i) * 1024,
-          live ? voff[i] : kOutOfRange, 0);
+    dma16(make_rsrc(base, bytes), dst + (CPW * wave + i) * 1024, live ? voff[i] : kOutOfRange,
+          0);
   }
   __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live) const {
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) copy_one(dst, kt, wave, live, i);
+    for (int i = 0; i < CPW; ++i) copy_one(dst, kt, wave, live, i);
+  }
+  // Stage kt (two bands) of the tile, from its first stage.
+  __device__ __forceinline__ void copy_at(uint32_t dst, int64_t kt, int wave, bool live,
+                                         int i) const {
+    const int64_t o = kt * 2 * band;
+    dma16(make_rsrc(base + o, bytes - o), dst + (CPW * wave + i) * 1024,
+          live ? voff[i] : kOutOfRange, 0);
   }
   // The second read is 4 k-rows further: 4 block rows, the same swizzle.
   __device__ __forceinline__ u32x4_t frag(const char* src, int mi) const {
@@ -505,7 +530,7 @@ template <> struct Side<__bf16, kMN> : SideMNb16<false> {};
 template <> struct Side<__bf16, kMNStep> : SideMNb16<true> {};
 template <> struct Side<float, kMN> : SideMNf32<false> {};
 template <> struct Side<float, kMNStep> : SideMNf32<true> {};
-template <> struct Side<__bf16, kMNBlkStep> : SideMNb16Blk {};
+template <> struct Side<__bf16, kMNBlkStep> : SideMNb16Blk<> {};
 
 // ---------------------------------------------------------------------------
 // MFMA on one 16-byte fragment pair.

@@ -36,8 +36,9 @@ constexpr int kRowBytes = kStageK * 2;           // 128
 constexpr int kOpBytes = kTile * kRowBytes;      // one operand's stage: 32 KiB
 constexpr int kStageBytes = 2 * kOpBytes;        // A and B: 64 KiB
 constexpr int kLdsBytes = 2 * kStageBytes;       // two stage buffers
+constexpr int kStagingBytes = 32 * 1024;         // epilogue staging after them (GEMMs only)
 constexpr int kLoads = kOpBytes / 16 / kThreads; // 16-byte loads per thread per operand per stage
-static_assert(kLoads == 8 && kLdsBytes <= 160 * 1024, "stage geometry");
+static_assert(kLoads == 8 && kLdsBytes + kStagingBytes <= 160 * 1024, "stage geometry");
 
 // Accumulators of one wave, with the wave shape the epilogues read.
 // The epilogues read it element by element through read(), which moves one
@@ -79,16 +80,28 @@ __device__ __forceinline__ void end_of_tile() {
 // whole rows).
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// One K-contiguous bf16 operand's stage copies, global -> LDS by LDS-DMA
-// (no registers): 32 wave-wide copies of 1 KiB per operand and stage, eight
-// per wave.  Copy i of wave w fills rows 8 c .. 8 c + 7, c = 8 w + i; lane l
-// fills physical chunk l % 8 of row 8 c + l / 8, i.e. reads the row's logical
-// chunk (l % 8) ^ swz(row).
-struct Copier {
+// Operand sides.  A side fills its operand's half of a stage buffer (kOpBytes
+// at dst) with copy i = 0..7 of this wave for stage kt of the tile it is
+// pointed at, and reads the fragment of 16-row (or 16-column) sub-tile mi for
+// K step ks of a stage at src:
+//   init(op, mn0, wave, lane, sub0)   per-lane offsets; sub0 = the wave's first
+//                                     row (column) in the tile
+//   retarget_if(op, mn0, yes)         point the copies at the tile at mn0 if
+//                                     yes (branch-free)
+//   copy(dst, kt, wave, live, i)      a dead copy (live == false) reads zeros
+//   frag(src, ks, mi)
+
+// K-contiguous bf16 operand kept as 256 rows of 128 bytes (both K steps of a
+// stage in one row).  Copy i of wave w fills rows 8 c .. 8 c + 7, c = 8 w + i;
+// lane l fills physical chunk l % 8 of row 8 c + l / 8, i.e. reads the row's
+// logical chunk (l % 8) ^ swz(row).  A fragment read: lane l reads row l % 16
+// of the sub-tile, logical chunk 4 ks + l / 16.
+struct KRow128 {
   u32x4_t rsrc;
   int64_t k_ext_bytes;
   uint32_t voff[kLoads];  // per copy: row * row_bytes + logical chunk * 16
   uint32_t kb[2];         // logical chunk bytes of even and odd copies
+  uint32_t off[2];        // per K step: this lane's fragment offset in sub-tile 0
 
   __device__ __forceinline__ void retarget(const Operand<__bf16>& op, int64_t mn0) {
     rsrc = make_rsrc(op.base + mn0 * op.ld, (op.mn_ext - mn0) * op.ld * 2);
@@ -98,7 +111,8 @@ struct Copier {
 #pragma unroll
     for (int q = 0; q < 4; ++q) rsrc[q] = yes ? r[q] : rsrc[q];
   }
-  __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane) {
+  __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane,
+                                       int sub0) {
     const int64_t row_bytes = op.ld * 2;
     k_ext_bytes = op.k_ext * 2;
 #pragma unroll
@@ -109,10 +123,12 @@ struct Copier {
       voff[i] = (uint32_t)(row * row_bytes + lc * 16);
       if (i < 2) kb[i] = (uint32_t)(lc * 16);  // swz(row) depends on c only through c & 1
     }
+    const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      off[ks] = (uint32_t)((sub0 + j) * kRowBytes + (((4 * ks + g) ^ swz(j)) * 16));
     retarget(op, mn0);
   }
-  // Copy i of stage kt of the current tile to the operand's stage at lds
-  // address dst (zeros past K, past the rows, and for a dead stage).
   __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live, int i) const {
     const int64_t k0 = kt * kRowBytes;
     const bool ok = live && k0 + kb[i & 1] < k_ext_bytes;
@@ -120,22 +136,45 @@ struct Copier {
     dma16(rsrc, dst + (kLoads * wave + i) * 1024, ok ? voff[i] : kOutOfRange,
           __builtin_amdgcn_readfirstlane(live ? (uint32_t)k0 : 0u));
   }
+  __device__ __forceinline__ u32x4_t frag(const char* src, int ks, int mi) const {
+    return *reinterpret_cast<const u32x4_t*>(src + off[ks] + mi * kMfma * kRowBytes);
+  }
 };
 
-// Fragment of 16-row sub-tile mi for K step ks (0, 1) of a stage: lane l reads
-// row l % 16 of the sub-tile, chunk 4 ks + l / 16.
-struct FragK {
-  uint32_t off[2];
-  __device__ __forceinline__ void init(int sub0, int lane) {
-    const int j = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      off[ks] = (uint32_t)((sub0 + j) * kRowBytes + (((4 * ks + g) ^ swz(j)) * 16));
+// An operand side of the eight-wave engine (tile_engine.h), built for four
+// copies per wave: its stages are one MFMA K step (kOperandBytes = 16 KiB), so
+// stage kt here is its stages 2 kt and 2 kt + 1, one after the other.  Copies
+// 0..3 of a wave fill the first, 4..7 the second.
+constexpr int kCopiesPerSub = kLoads / 2;
+template <typename S>
+struct Pair {
+  S s;
+  int64_t mn0;  // the tile the copies point at
+  static_assert(2 * kOperandBytes == kOpBytes, "two stages of the eight-wave engine per stage");
+  __device__ __forceinline__ void retarget_if(const Operand<__bf16>& op, int64_t next, bool yes) {
+    mn0 = yes ? next : mn0;
+    s.retarget(op, mn0);
   }
-  __device__ __forceinline__ u32x4_t read(const char* op_stage, int ks, int mi) const {
-    return *reinterpret_cast<const u32x4_t*>(op_stage + off[ks] + mi * kMfma * kRowBytes);
+  __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t first, int wave, int lane,
+                                       int sub0) {
+    mn0 = first;
+    s.init(op, first, wave, lane, sub0);
+  }
+  __device__ __forceinline__ void copy(uint32_t dst, int64_t kt, int wave, bool live, int i) const {
+    const int h = i / kCopiesPerSub;
+    s.copy_at(dst + h * kOperandBytes, 2 * kt + h, wave, live, i % kCopiesPerSub);
+  }
+  __device__ __forceinline__ u32x4_t frag(const char* src, int ks, int mi) const {
+    return s.frag(src + ks * kOperandBytes, mi);
   }
 };
+
+// The eight-wave engine's layouts with four copies per wave: K-contiguous
+// gradient strip in blocks (split placement), MN-contiguous bf16 (descriptor
+// computed per stage), and the blocked MN-contiguous gradient strip.
+using KSplitBlk = Pair<SideK<__bf16, true, true, kCopiesPerSub>>;
+using MN = Pair<SideMNb16<false, kCopiesPerSub>>;
+using MNBlk = Pair<SideMNb16Blk<kCopiesPerSub>>;
 
 // Until every copy and LDS access of this wave is done (vmcnt(0) lgkmcnt(0)).
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0070); }
@@ -147,9 +186,9 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0070);
 //          last half);
 //   h = 1: reads a[0..4) of the next K step (free since half 0) and each b[ni]
 //          of the next K step right after its last MFMA here.
-template <int H, bool First, typename CopyFn>
+template <int H, bool First, typename SA, typename SB, typename CopyFn>
 __device__ __forceinline__ void half_step(Acc& acc, u32x4_t (&a)[kMI], u32x4_t (&b)[kNI],
-                                          const FragK& fa, const FragK& fb, const char* a_src,
+                                          const SA& sa, const SB& sb, const char* a_src,
                                           const char* b_src, int ks_read, int n_copies,
                                           CopyFn&& copy_fn) {
 #pragma unroll
@@ -160,10 +199,10 @@ __device__ __forceinline__ void half_step(Acc& acc, u32x4_t (&a)[kMI], u32x4_t (
     else
       mfma_acc(acc.c[mi][ni], a[mi], b[ni]);
     if constexpr (H == 0) {
-      if (t < 4) a[4 + t] = fa.read(a_src, ks_read, 4 + t);
+      if (t < 4) a[4 + t] = sa.frag(a_src, ks_read, 4 + t);
     } else {
-      if (t % 4 == 3) b[ni] = fb.read(b_src, ks_read, ni);
-      else if (t < 5) a[t < 3 ? t : t - 1] = fa.read(a_src, ks_read, t < 3 ? t : t - 1);
+      if (t % 4 == 3) b[ni] = sb.frag(b_src, ks_read, ni);
+      else if (t < 5) a[t < 3 ? t : t - 1] = sa.frag(a_src, ks_read, t < 3 ? t : t - 1);
     }
     if (t % 4 == 1 && t / 4 < n_copies) copy_fn(t / 4);
     sched_fence();
@@ -171,8 +210,9 @@ __device__ __forceinline__ void half_step(Acc& acc, u32x4_t (&a)[kMI], u32x4_t (
 }
 
 // Every tile of this block: C[m0:m0+256, n0:n0+256] = sum_k A[m, k] B[n, k]
-// over k < k_len, then epi(acc, m0, n0).  Needs at least two K stages per
-// tile (the copy stream runs at most one tile ahead).
+// over k < k_len, then epi(acc, m0, n0, staging), where staging is the
+// kStagingBytes of LDS past the two stage buffers.  Needs at least two K
+// stages per tile (the copy stream runs at most one tile ahead).
 //
 // Stage q lives in buffer q % 2 and has two K steps; with the MFMAs at stage q:
 //   half 0 of step 0:  reads a[4..8) of step 0; copies 8..15 of stage q + 1
@@ -183,8 +223,10 @@ __device__ __forceinline__ void half_step(Acc& acc, u32x4_t (&a)[kMI], u32x4_t (
 //   half 1 of step 1:  reads a[0..4) and b of stage q + 1's step 0 from the
 //                      other buffer; copies 0..7 of stage q + 2 into buffer q.
 // A buffer is written only after the barrier that follows its last reads, and
-// read only after the barrier that follows its copies' completion.
-template <typename Epi>
+// read only after the barrier that follows its copies' completion.  The
+// epilogue's loads and stores are waited for with the copies at the next
+// barrier.
+template <typename SA, typename SB, typename Epi>
 __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operand<__bf16>& B,
                                           int64_t k_len, const TileGrid& grid, char* lds,
                                           Epi&& epi) {
@@ -193,6 +235,7 @@ __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operan
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const uint32_t lds0 = lds_addr(lds);
+  char* const staging = lds + kLdsBytes;
   const int64_t nk = (k_len + kStageK - 1) / kStageK;
   const int64_t tiles = grid.count();
   if (tiles == 0) return;
@@ -203,30 +246,29 @@ __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operan
   next_n0 = n0;
   if (tiles > 1) grid.coords(1, &next_m0, &next_n0);
 
-  Copier ca, cb;
-  ca.init(A, m0, wave, lane);
-  cb.init(B, n0, wave, lane);
-  FragK fa, fb;
-  fa.init(wm * kWaveM, lane);
-  fb.init(wn * kWaveN, lane);
+  SA sa;
+  SB sb;
+  sa.init(A, m0, wave, lane, wm * kWaveM);
+  sb.init(B, n0, wave, lane, wn * kWaveN);
 
-  // copy stream: stage ck of the block's tile ct; copy i < 8 is A's, else B's
-  // (branch-free, so that a stage is one basic block: a branch in the loop
-  // made the register allocator shuttle accumulators between AGPRs and VGPRs)
+  // copy stream: stage ck of the block's tile ct; copy i < 8 is A's, else
+  // B's.  Branch-free, so that a stage is one basic block: a branch in the
+  // loop made the register allocator shuttle accumulators between AGPRs and
+  // VGPRs.
   int64_t ct = 0, ck = 0;
   auto advance = [&]() {
     const bool wrap = ++ck == nk;
     ck = wrap ? 0 : ck;
     ct += wrap ? 1 : 0;
     // the stream is at most one tile ahead of the MFMAs: tile ct is the next one
-    ca.retarget_if(A, next_m0, wrap);
-    cb.retarget_if(B, next_n0, wrap);
+    sa.retarget_if(A, next_m0, wrap);
+    sb.retarget_if(B, next_n0, wrap);
   };
   auto copy_one = [&](uint32_t buf_addr, int i) {
     if (i < kLoads)
-      ca.copy(buf_addr, ck, wave, ct < tiles, i);
+      sa.copy(buf_addr, ck, wave, ct < tiles, i);
     else
-      cb.copy(buf_addr + kOpBytes, ck, wave, ct < tiles, i - kLoads);
+      sb.copy(buf_addr + kOpBytes, ck, wave, ct < tiles, i - kLoads);
   };
 
   // stage 0 into buffer 0, the first half of stage 1 into buffer 1
@@ -241,9 +283,9 @@ __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operan
   Acc acc;
   u32x4_t a[kMI], b[kNI];
 #pragma unroll
-  for (int i = 0; i < kMI / 2; ++i) a[i] = fa.read(lds, 0, i);
+  for (int i = 0; i < kMI / 2; ++i) a[i] = sa.frag(lds, 0, i);
 #pragma unroll
-  for (int i = 0; i < kNI; ++i) b[i] = fb.read(lds + kOpBytes, 0, i);
+  for (int i = 0; i < kNI; ++i) b[i] = sb.frag(lds + kOpBytes, 0, i);
   uint32_t buf = 0;
 
   for (int64_t t = 0; t < tiles; ++t) {
@@ -257,19 +299,19 @@ __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operan
       auto copy_b = [&](int i) { copy_one(nxt_addr, kLoads + i); };
       auto copy_a = [&](int i) { copy_one(cur_addr, i); };
       auto none = [&](int) {};
-      half_step<0, kFirst>(acc, a, b, fa, fb, cur, cur + kOpBytes, 0, kLoads, copy_b);
+      half_step<0, kFirst>(acc, a, b, sa, sb, cur, cur + kOpBytes, 0, kLoads, copy_b);
       advance();
-      half_step<1, kFirst>(acc, a, b, fa, fb, cur, cur + kOpBytes, 1, 0, none);
-      half_step<0, false>(acc, a, b, fa, fb, cur, cur + kOpBytes, 1, 0, none);
+      half_step<1, kFirst>(acc, a, b, sa, sb, cur, cur + kOpBytes, 1, 0, none);
+      half_step<0, false>(acc, a, b, sa, sb, cur, cur + kOpBytes, 1, 0, none);
       wait_all();
       block_barrier();
-      half_step<1, false>(acc, a, b, fa, fb, nxt, nxt + kOpBytes, 0, kLoads, copy_a);
+      half_step<1, false>(acc, a, b, sa, sb, nxt, nxt + kOpBytes, 0, kLoads, copy_a);
       buf ^= 1;
     };
     stage(std::true_type{});
     for (int64_t kt = 1; kt < nk; ++kt) stage(std::false_type{});
     end_of_tile();
-    epi(acc, m0, n0);
+    epi(acc, m0, n0, staging);
     m0 = next_m0;
     n0 = next_n0;
     if (t + 2 < tiles) grid.coords(t + 2, &next_m0, &next_n0);
