@@ -167,6 +167,9 @@ SMALL = [
             target_law="zipf", ignore_frac=0.05),
     # a vocabulary tail of 40 rows, 5 tokens in the last band of 16
     S.small("bf16_w4_short_tails", 517, 1088, 552, 512, ignore_frac=0.1),
+    # at least 8 tiles per block (17 x 122 tiles in one strip): the gradient
+    # strip's late copy schedule
+    S.small("bf16_w4_late_copies", 4160, 1024, 31000, 31000, ignore_frac=0.1),
 ]
 
 

@@ -114,14 +114,16 @@ __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, AccT& acc, i
   }
 }
 
-// The forward strip on the one-wave-per-SIMD engine (bf16).
+// The forward strip on the one-wave-per-SIMD engine (bf16); Late: the copy
+// schedule of w4::run_tiles for blocks with many tiles.
+template <bool Late>
 __global__ __launch_bounds__(w4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void strip_lse_kernel_w4(StripArgs<__bf16> a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const Operand<__bf16> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<__bf16> B{a.hidden, a.H, a.N, a.H};
   const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
-  w4::run_tiles<w4::KRow128, w4::KRow128>(A, B, a.H, grid, lds,
+  w4::run_tiles<w4::KRow128, w4::KRow128, Late>(A, B, a.H, grid, lds,
                                           [&](w4::Acc& acc, int64_t m0, int64_t n0, char*) {
                                             lse_epilogue(a, acc, m0, n0);
                                           });
@@ -482,13 +484,14 @@ __device__ __forceinline__ void grad_epilogue_blocked(const StripArgs<__bf16>& a
 }
 
 // The backward strip on the one-wave-per-SIMD engine (bf16, blocked G).
+template <bool Late>
 __global__ __launch_bounds__(w4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void strip_grad_kernel_w4(StripArgs<__bf16> a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const Operand<__bf16> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<__bf16> B{a.hidden, a.H, a.N, a.H};
   const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
-  w4::run_tiles<w4::KRow128, w4::KRow128>(A, B, a.H, grid, lds,
+  w4::run_tiles<w4::KRow128, w4::KRow128, Late>(A, B, a.H, grid, lds,
                                           [&](w4::Acc& acc, int64_t m0, int64_t n0, char*) {
                                             grad_epilogue_blocked(a, acc, m0, n0);
                                           });
@@ -1103,14 +1106,21 @@ static int64_t stages_of(int64_t k_len) {
 }
 
 // A strip kernel on the one-wave-per-SIMD engine, in persistent blocks (its
-// copy stream needs at least two K stages per tile).
-static hipError_t launch_w4(void (*kernel)(StripArgs<__bf16>), const StripArgs<__bf16>& a,
-                            hipStream_t st) {
+// copy stream needs at least two K stages per tile).  The gradient strip
+// takes the late copy schedule (both operands' copies of a stage in the last
+// half step two stages ahead) when its blocks have at least 8 tiles: at
+// 131072 tokens, 64 tiles per block, it was 0.7-1.2% faster on four boxes;
+// at 4096 tokens, 2 tiles per block, 2.5-4% slower.  The forward keeps the
+// default schedule (with the late one: within noise at 131072 tokens, up to
+// 2.4% slower at 4096 with 37 tiles per block).
+static hipError_t launch_w4(void (*early)(StripArgs<__bf16>), void (*late)(StripArgs<__bf16>),
+                            const StripArgs<__bf16>& a, hipStream_t st) {
   if (cdiv(a.H, w4::kStageK) < 2) return hipErrorInvalidValue;
   const int64_t tiles = a.m_tiles * a.n_tiles;
   const int64_t p = persistent_blocks();
   const int64_t blocks = tiles < p ? tiles : p;
   if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
+  void (*kernel)(StripArgs<__bf16>) = late && tiles >= 8 * blocks ? late : early;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, w4::kLdsBytes);
   if (e != hipSuccess) return e;
@@ -1140,7 +1150,7 @@ hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st) {
   a.n_tiles = cdiv(a.N, kTile);
   a.group_m = kStripGroupM;
   if constexpr (std::is_same<T, __bf16>::value)
-    if (use_w4(a)) return launch_w4(strip_lse_kernel_w4, a, st);
+    if (use_w4(a)) return launch_w4(strip_lse_kernel_w4<false>, nullptr, a, st);
   const int64_t blocks = grid_blocks(a.m_tiles * a.n_tiles, stages_of<T>(a.H));
   if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_lse_kernel<T>));
@@ -1155,7 +1165,8 @@ hipError_t launch_strip_grad(StripArgs<T> a, hipStream_t st) {
   a.n_tiles = cdiv(a.N, kTile);
   a.group_m = kStripGroupM;
   if constexpr (std::is_same<T, __bf16>::value)
-    if (use_w4(a)) return launch_w4(strip_grad_kernel_w4, a, st);
+    if (use_w4(a))
+      return launch_w4(strip_grad_kernel_w4<false>, strip_grad_kernel_w4<true>, a, st);
   const int64_t blocks = grid_blocks(a.m_tiles * a.n_tiles, stages_of<T>(a.H));
   if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_grad_kernel<T>));

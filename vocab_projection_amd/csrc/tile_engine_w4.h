@@ -181,12 +181,13 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0070);
 
 // Half h of K step ks: the MFMAs of sub-tiles mi in [4 h, 4 h + 4) for every
 // ni, ni-major, each followed (per the caller's plan) by one fragment read and
-// at most one stage copy, in program order (scheduling fences keep it).
+// at most one stage copy (after MFMAs 1, 1 + Gap, ...), in program order
+// (scheduling fences keep it).
 //   h = 0: reads a[4..8) of this K step (their registers were freed by the
 //          last half);
 //   h = 1: reads a[0..4) of the next K step (free since half 0) and each b[ni]
 //          of the next K step right after its last MFMA here.
-template <int H, bool First, typename SA, typename SB, typename CopyFn>
+template <int H, bool First, int Gap = 4, typename SA, typename SB, typename CopyFn>
 __device__ __forceinline__ void half_step(Acc& acc, u32x4_t (&a)[kMI], u32x4_t (&b)[kNI],
                                           const SA& sa, const SB& sb, const char* a_src,
                                           const char* b_src, int ks_read, int n_copies,
@@ -204,7 +205,7 @@ __device__ __forceinline__ void half_step(Acc& acc, u32x4_t (&a)[kMI], u32x4_t (
       if (t % 4 == 3) b[ni] = sb.frag(b_src, ks_read, ni);
       else if (t < 5) a[t < 3 ? t : t - 1] = sa.frag(a_src, ks_read, t < 3 ? t : t - 1);
     }
-    if (t % 4 == 1 && t / 4 < n_copies) copy_fn(t / 4);
+    if (t % Gap == 1 && t / Gap < n_copies) copy_fn(t / Gap);
     sched_fence();
   }
 }
@@ -215,18 +216,24 @@ __device__ __forceinline__ void half_step(Acc& acc, u32x4_t (&a)[kMI], u32x4_t (
 // stages per tile (the copy stream runs at most one tile ahead).
 //
 // Stage q lives in buffer q % 2 and has two K steps; with the MFMAs at stage q:
-//   half 0 of step 0:  reads a[4..8) of step 0; copies 8..15 of stage q + 1
-//                      into the other buffer (0..7 were issued before);
+//   half 0 of step 0:  reads a[4..8) of step 0; B's copies of stage q + 1
+//                      into the other buffer, one per four MFMAs (A's were
+//                      issued before) - unless Late;
 //   half 1 of step 0:  reads a[0..4) and b of step 1;
 //   half 0 of step 1:  reads a[4..8) of step 1 (the last reads of buffer q);
 //   wait for every copy (stage q + 1's) and read; barrier;
 //   half 1 of step 1:  reads a[0..4) and b of stage q + 1's step 0 from the
-//                      other buffer; copies 0..7 of stage q + 2 into buffer q.
-// A buffer is written only after the barrier that follows its last reads, and
-// read only after the barrier that follows its copies' completion.  The
-// epilogue's loads and stores are waited for with the copies at the next
-// barrier.
-template <typename SA, typename SB, typename Epi>
+//                      other buffer; A's copies of stage q + 2 into buffer q,
+//                      one per four MFMAs, or with Late both operands'
+//                      copies, one per two MFMAs.
+// Late gives B's copies a whole stage of lead instead of half of one: the
+// gradient strip with many tiles per block gains from it (1%), with two
+// tiles per block it loses (3%), and dW (MN-contiguous operands, a
+// descriptor computed per copy) loses 6%.  A buffer is written
+// only after the barrier that follows its last reads, and read only after
+// the barrier that follows its copies' completion.  The epilogue's loads and
+// stores are waited for with the copies at the next barrier.
+template <typename SA, typename SB, bool Late = false, typename Epi>
 __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operand<__bf16>& B,
                                           int64_t k_len, const TileGrid& grid, char* lds,
                                           Epi&& epi) {
@@ -271,13 +278,15 @@ __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operan
       sb.copy(buf_addr + kOpBytes, ck, wave, ct < tiles, i - kLoads);
   };
 
-  // stage 0 into buffer 0, the first half of stage 1 into buffer 1
+  // stage 0 into buffer 0; stage 1 (Late), or A's half of it, into buffer 1
+  constexpr int kAhead = Late ? 2 * kLoads : kLoads;  // copies of stage 1
 #pragma unroll
   for (int i = 0; i < 2 * kLoads; ++i) copy_one(lds0, i);
   advance();
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) copy_one(lds0 + kStageBytes, i);
-  __builtin_amdgcn_s_waitcnt((kLoads) | (7 << 4) | (0 << 8));  // stage 0 landed (vmcnt(8))
+  for (int i = 0; i < kAhead; ++i) copy_one(lds0 + kStageBytes, i);
+  if constexpr (Late) advance();
+  __builtin_amdgcn_s_waitcnt((kAhead & 15) | ((kAhead >> 4) << 14) | (7 << 4));  // stage 0 landed
   block_barrier();
 
   Acc acc;
@@ -297,15 +306,17 @@ __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operan
       const uint32_t cur_addr = lds0 + buf * kStageBytes;
       const uint32_t nxt_addr = lds0 + (buf ^ 1) * kStageBytes;
       auto copy_b = [&](int i) { copy_one(nxt_addr, kLoads + i); };
-      auto copy_a = [&](int i) { copy_one(cur_addr, i); };
+      auto copy_a = [&](int i) { copy_one(cur_addr, i); };  // i >= kLoads: B's (Late)
       auto none = [&](int) {};
-      half_step<0, kFirst>(acc, a, b, sa, sb, cur, cur + kOpBytes, 0, kLoads, copy_b);
-      advance();
+      half_step<0, kFirst>(acc, a, b, sa, sb, cur, cur + kOpBytes, 0, Late ? 0 : kLoads, copy_b);
+      if constexpr (!Late) advance();
       half_step<1, kFirst>(acc, a, b, sa, sb, cur, cur + kOpBytes, 1, 0, none);
       half_step<0, false>(acc, a, b, sa, sb, cur, cur + kOpBytes, 1, 0, none);
       wait_all();
       block_barrier();
-      half_step<1, false>(acc, a, b, sa, sb, nxt, nxt + kOpBytes, 0, kLoads, copy_a);
+      half_step<1, false, Late ? 2 : 4>(acc, a, b, sa, sb, nxt, nxt + kOpBytes, 0,
+                                        Late ? 2 * kLoads : kLoads, copy_a);
+      if constexpr (Late) advance();
       buf ^= 1;
     };
     stage(std::true_type{});
