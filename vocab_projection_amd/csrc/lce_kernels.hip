@@ -39,19 +39,61 @@ template <> constexpr bool kGBlocked<__bf16> = true;
 // ---------------------------------------------------------------------------
 // Forward strip: MFMA M = vocabulary rows of the strip, N = tokens, K = H.
 // ---------------------------------------------------------------------------
+// The combination of x over the lanes l, l ^ 16, l ^ 32 and l ^ 48 (one
+// token's four row groups), in every lane, by row swaps on the VALU: after
+// v_permlane16_swap of two copies of x, lane by lane one copy holds x of the
+// even and the other x of the odd row of a row pair, and after
+// v_permlane32_swap x of the lower and of the upper half, so op of the two is
+// the xor-16 and then the xor-32 combination (the same operands, in either
+// order, as exchanges through ds_bpermute, without their LDS round trips).
+// The swaps are written as assembly: through the builtin, the optimiser
+// replaced the second result by the first in this use.  The s_nop covers the
+// wait states between the VALU write of an operand and the swap that the
+// compiler itself places before these instructions.
+template <typename Op>
+__device__ __forceinline__ float combine_row_groups(float x, Op op) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  float c = op(a, b), d = c;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
+  return op(c, d);
+}
+
+// The token of column block ni of a tile that this lane's values belong to.
+template <typename AccT>
+__device__ __forceinline__ int64_t lse_token(int64_t n0, int ni) {
+  const int tid = (int)threadIdx.x;
+  return n0 + (__builtin_amdgcn_readfirstlane(tid >> 6) >> 1) * AccT::WaveN + ni * kMfma + (tid & 15);
+}
+
+// The targets of this lane's tokens of a tile, read at the token clamped to
+// N - 1 (the caller drops tokens past N): an unconditional load goes straight
+// to its register, where a guarded one was followed by a select that waited
+// for it.
+template <typename T, typename AccT>
+__device__ __forceinline__ void lse_targets(const StripArgs<T>& a, int64_t n0,
+                                            int32_t (&tgt)[AccT::NI]) {
+#pragma unroll
+  for (int ni = 0; ni < AccT::NI; ++ni) {
+    const int64_t tok = lse_token<AccT>(n0, ni);
+    tgt[ni] = a.targets[tok < a.N ? tok : a.N - 1];
+  }
+}
+
 // Per token of the tile and per 128 strip rows of a wave: (max, sum of
 // exp(z - max)) to partials, and the target logit to z_target.  A token's
 // 128 rows of a wave sit in the four lanes l % 16 + 16 h (h = 0..3), 32
-// values each.
+// values each.  tgt: the tokens' targets, loaded before the tile's stages
+// (pre), or null to load them here, all before the first use.
 template <typename T, typename AccT>
 __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, AccT& acc, int64_t m0,
-                                             int64_t n0) {
-  constexpr int kMI = AccT::MI, kNI = AccT::NI, kWaveM = AccT::WaveM, kWaveN = AccT::WaveN;
+                                             int64_t n0, const int32_t* pre_tgt = nullptr) {
+  constexpr int kMI = AccT::MI, kNI = AccT::NI, kWaveM = AccT::WaveM;
   // lane values recomputed per tile rather than hoisted and kept live
   const int tid = opaque((int)threadIdx.x);
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1;
   const int64_t vrow0 = m0 + wm * kWaveM;             // first strip row of this wave
   const int64_t rows_left = a.v_len - vrow0;
   if (rows_left <= 0) return;                          // wave-uniform
@@ -60,12 +102,19 @@ __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, AccT& acc, i
   const int64_t blk = vrow0 / kWaveM;
   const int r_lane = (lane >> 4) * 4;  // acc_row(mi, e, lane) - acc_row(mi, e, 0)
 
+  int32_t tgt[kNI];
+  if (pre_tgt) {
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) tgt[ni] = pre_tgt[ni];
+  } else {
+    lse_targets<T, AccT>(a, n0, tgt);
+  }
+
   // One 16-token column block (ni) at a time, so that only its 32 values per
   // lane are held in VGPRs.
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
-    const int64_t tok = n0 + wn * kWaveN + ni * kMfma + (lane & 15);
-    const bool tok_ok = tok < a.N;
+    const int64_t tok = lse_token<AccT>(n0, ni);
     float v[4 * kMI];
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
@@ -82,18 +131,15 @@ __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, AccT& acc, i
     float mx = -INFINITY;
 #pragma unroll
     for (int q = 0; q < 4 * kMI; ++q) mx = fmaxf(mx, v[q]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = combine_row_groups(mx, [](float x, float y) { return fmaxf(x, y); });
     const float mscaled = mx * kLog2e;
     float sum = 0.f;
 #pragma unroll
     for (int q = 0; q < 4 * kMI; ++q) sum += fast_exp2(__builtin_fmaf(v[q], kLog2e, -mscaled));
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
-    if (lane < 16 && tok_ok) a.partials[blk * a.N + tok] = float2{mx, sum};
+    sum = combine_row_groups(sum, [](float x, float y) { return x + y; });
 
     // Target logit: at most one (row, token) pair of the whole strip matches.
-    const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
+    const int32_t t = tok < a.N ? tgt[ni] : a.ignore_index;
     const int64_t local = (int64_t)t - (a.v_begin + vrow0);
     const bool hit = t != a.ignore_index && local >= 0 && local < nrows;
     if (__any(hit)) {
@@ -110,6 +156,7 @@ __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, AccT& acc, i
         }
       if (mine) a.z_target[tok] = zt;
     }
+    if (lane < 16 && tok < a.N) a.partials[blk * a.N + tok] = float2{mx, sum};
     sched_fence();
   }
 }
@@ -123,10 +170,11 @@ void strip_lse_kernel_w4(StripArgs<__bf16> a) {
   const Operand<__bf16> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<__bf16> B{a.hidden, a.H, a.N, a.H};
   const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
-  w4::run_tiles<w4::KRow128, w4::KRow128, Late>(A, B, a.H, grid, lds,
-                                          [&](w4::Acc& acc, int64_t m0, int64_t n0, char*) {
-                                            lse_epilogue(a, acc, m0, n0);
-                                          });
+  int32_t tgt[w4::kNI];  // loaded at a tile's start, used by its epilogue
+  w4::run_tiles<w4::KRow128, w4::KRow128, Late>(
+      A, B, a.H, grid, lds,
+      [&](int64_t, int64_t n0) { lse_targets<__bf16, w4::Acc>(a, n0, tgt); },
+      [&](w4::Acc& acc, int64_t m0, int64_t n0, char*) { lse_epilogue(a, acc, m0, n0, tgt); });
 }
 
 template <typename T>
@@ -393,9 +441,35 @@ __device__ __forceinline__ void grad_epilogue(const StripArgs<__bf16>& a, Acc& a
 // packed dword gives every lane 16 contiguous bytes of a block row (groups 0
 // and 2 the first tile's halves, groups 1 and 3 the second's).  Targets and
 // lse are loaded before any store.
+// What the gradient epilogue reads per token of a tile (targets, lse) and the
+// gradient scale: loaded before the tile's stages, so that the epilogue does
+// not wait on them (nor on the copies in flight that such a wait would drain).
+template <typename AccT>
+struct GradInputs {
+  int32_t tgt[AccT::NI];
+  float lse[AccT::NI];
+  float scale;
+};
+
+// (Read at the token clamped to N - 1, as in lse_targets; the epilogue drops
+// tokens past N.)
+template <typename AccT>
+__device__ __forceinline__ void grad_inputs(const StripArgs<__bf16>& a, int64_t n0,
+                                            GradInputs<AccT>& in) {
+#pragma unroll
+  for (int ni = 0; ni < AccT::NI; ++ni) {
+    const int64_t tok = lse_token<AccT>(n0, ni);
+    const int64_t tc = tok < a.N ? tok : a.N - 1;
+    in.tgt[ni] = a.targets[tc];
+    in.lse[ni] = a.lse[tc];
+  }
+  in.scale = a.ctrl->grad_scale;
+}
+
 template <typename AccT>
 __device__ __forceinline__ void grad_epilogue_blocked(const StripArgs<__bf16>& a, AccT& acc,
-                                                      int64_t m0, int64_t n0) {
+                                                      int64_t m0, int64_t n0,
+                                                      const GradInputs<AccT>* pre = nullptr) {
   constexpr int kMI = AccT::MI, kNI = AccT::NI, kWaveM = AccT::WaveM, kWaveN = AccT::WaveN;
   const int tid = opaque((int)threadIdx.x);  // recomputed per tile, not kept live
   const int lane = tid & 63;
@@ -405,7 +479,12 @@ __device__ __forceinline__ void grad_epilogue_blocked(const StripArgs<__bf16>& a
   const bool full = vrow0 + kWaveM <= a.v_len;
   const int rows_left = full ? kWaveM : (int)max<int64_t>(a.v_len - vrow0, 0);
   const int r_lane = (lane >> 4) * 4;
-  const float scale_all = a.ctrl->grad_scale;
+  GradInputs<AccT> in;
+  if (pre)
+    in = *pre;
+  else
+    grad_inputs<AccT>(a, n0, in);
+  const float scale_all = in.scale;
   const float abs_scale = fabsf(scale_all);
   const uint32_t sign = scale_all < 0.f ? 0x80008000u : 0u;
   const float log2_scale = __builtin_amdgcn_logf(abs_scale);
@@ -415,11 +494,10 @@ __device__ __forceinline__ void grad_epilogue_blocked(const StripArgs<__bf16>& a
   bool any_hit[kNI];
 #pragma unroll
   for (int ni = 0; ni < kNI; ++ni) {
-    const int64_t tok = n0 + wn * kWaveN + ni * kMfma + (lane & 15);
-    const bool tok_ok = tok < a.N;
-    const int32_t t = tok_ok ? a.targets[tok] : a.ignore_index;
+    const bool tok_ok = lse_token<AccT>(n0, ni) < a.N;
+    const int32_t t = tok_ok ? in.tgt[ni] : a.ignore_index;
     const bool valid = t != a.ignore_index;
-    const float lse2 = (tok_ok ? a.lse[tok] : 0.f) * kLog2e;
+    const float lse2 = (tok_ok ? in.lse[ni] : 0.f) * kLog2e;
     c[ni] = valid ? log2_scale - lse2 : -INFINITY;
     const int64_t tl64 = (int64_t)t - (a.v_begin + vrow0);
     const bool hit = valid && tl64 >= 0 && tl64 < kWaveM;
@@ -491,10 +569,12 @@ void strip_grad_kernel_w4(StripArgs<__bf16> a) {
   const Operand<__bf16> A{a.weight_strip, a.H, a.v_len, a.H};
   const Operand<__bf16> B{a.hidden, a.H, a.N, a.H};
   const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
-  w4::run_tiles<w4::KRow128, w4::KRow128, Late>(A, B, a.H, grid, lds,
-                                          [&](w4::Acc& acc, int64_t m0, int64_t n0, char*) {
-                                            grad_epilogue_blocked(a, acc, m0, n0);
-                                          });
+  GradInputs<w4::Acc> in;  // loaded at a tile's start, used by its epilogue
+  w4::run_tiles<w4::KRow128, w4::KRow128, Late>(
+      A, B, a.H, grid, lds, [&](int64_t, int64_t n0) { grad_inputs<w4::Acc>(a, n0, in); },
+      [&](w4::Acc& acc, int64_t m0, int64_t n0, char*) {
+        grad_epilogue_blocked(a, acc, m0, n0, &in);
+      });
 }
 
 template <typename T>
@@ -701,7 +781,7 @@ void gemm_f32out_kernel_w4(GemmArgs<__bf16> g) {
   const Operand<__bf16> B{g.b, g.ldb, g.b_mn_ext, g.b_k_ext};
   const TileGrid grid{g.m_tiles, g.n_tiles, g.group_m, blockIdx.x, gridDim.x, kGemmBands};
   using SA = typename std::conditional<AK, w4::KSplitBlk, w4::MNBlk>::type;
-  w4::run_tiles<SA, w4::MN>(A, B, g.k_len, grid, lds,
+  w4::run_tiles<SA, w4::MN>(A, B, g.k_len, grid, lds, [](int64_t, int64_t) {},
                             [&](w4::Acc& acc, int64_t m0, int64_t n0, char* staging) {
                               gemm_epilogue_w4<__bf16, Accum>(g, acc, m0, n0, staging);
                             });
@@ -719,7 +799,7 @@ void gemm_dh_dw_kernel_w4(GemmArgs<__bf16> dh, GemmArgs<__bf16> dw, int64_t spli
     const Operand<__bf16> B{dh.b, dh.ldb, dh.b_mn_ext, dh.b_k_ext};
     const TileGrid grid{dh.m_tiles, dh.n_tiles, dh.group_m, b, split, kGemmBands};
     w4::run_tiles<w4::KSplitBlk, w4::MN>(
-        A, B, dh.k_len, grid, lds, [&](w4::Acc& acc, int64_t m0, int64_t n0, char* staging) {
+        A, B, dh.k_len, grid, lds, [](int64_t, int64_t) {}, [&](w4::Acc& acc, int64_t m0, int64_t n0, char* staging) {
           gemm_epilogue_w4<__bf16, AccumDh>(dh, acc, m0, n0, staging);
         });
   } else {
@@ -728,7 +808,7 @@ void gemm_dh_dw_kernel_w4(GemmArgs<__bf16> dh, GemmArgs<__bf16> dw, int64_t spli
     const TileGrid grid{dw.m_tiles, dw.n_tiles, dw.group_m, b - split, gridDim.x - split,
                         kGemmBands};
     w4::run_tiles<w4::MNBlk, w4::MN>(
-        A, B, dw.k_len, grid, lds, [&](w4::Acc& acc, int64_t m0, int64_t n0, char* staging) {
+        A, B, dw.k_len, grid, lds, [](int64_t, int64_t) {}, [&](w4::Acc& acc, int64_t m0, int64_t n0, char* staging) {
           gemm_epilogue_w4<__bf16, AccumDw>(dw, acc, m0, n0, staging);
         });
   }

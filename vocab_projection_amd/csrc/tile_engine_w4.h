@@ -210,10 +210,11 @@ __device__ __forceinline__ void half_step(Acc& acc, u32x4_t (&a)[kMI], u32x4_t (
   }
 }
 
-// Every tile of this block: C[m0:m0+256, n0:n0+256] = sum_k A[m, k] B[n, k]
-// over k < k_len, then epi(acc, m0, n0, staging), where staging is the
-// kStagingBytes of LDS past the two stage buffers.  Needs at least two K
-// stages per tile (the copy stream runs at most one tile ahead).
+// Every tile of this block: pre(m0, n0) (loads that the epilogue needs, which
+// then complete under the tile's stages), C[m0:m0+256, n0:n0+256] = sum_k
+// A[m, k] B[n, k] over k < k_len, then epi(acc, m0, n0, staging), where
+// staging is the kStagingBytes of LDS past the two stage buffers.  Needs at
+// least two K stages per tile (the copy stream runs at most one tile ahead).
 //
 // Stage q lives in buffer q % 2 and has two K steps; with the MFMAs at stage q:
 //   half 0 of step 0:  reads a[4..8) of step 0; B's copies of stage q + 1
@@ -233,10 +234,10 @@ __device__ __forceinline__ void half_step(Acc& acc, u32x4_t (&a)[kMI], u32x4_t (
 // only after the barrier that follows its last reads, and read only after
 // the barrier that follows its copies' completion.  The epilogue's loads and
 // stores are waited for with the copies at the next barrier.
-template <typename SA, typename SB, bool Late = false, typename Epi>
+template <typename SA, typename SB, bool Late = false, typename Pre, typename Epi>
 __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operand<__bf16>& B,
                                           int64_t k_len, const TileGrid& grid, char* lds,
-                                          Epi&& epi) {
+                                          Pre&& pre, Epi&& epi) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -319,6 +320,7 @@ __device__ __forceinline__ void run_tiles(const Operand<__bf16>& A, const Operan
       if constexpr (Late) advance();
       buf ^= 1;
     };
+    pre(m0, n0);
     stage(std::true_type{});
     for (int64_t kt = 1; kt < nk; ++kt) stage(std::false_type{});
     end_of_tile();
