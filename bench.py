@@ -248,15 +248,17 @@ def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, 
     the backward runs strip_grad, then dH and dW as two launches or as the one
     shared launch that lce_backward_fold makes for that strip."""
     # bf16 GEMMs with K >= 1024 run on the one-wave-per-SIMD engine: the strip
-    # kernels (K = H), dW (K = tokens) and the shared dH + dW launch
+    # kernels (K = H), dH (K = strip rows), dW (K = tokens) and the shared
+    # dH + dW launch
     bf16 = w.dtype == "bf16"
     w4 = "_w4" if bf16 and w.hidden >= 1024 else f"<{'bf16' if bf16 else 'float'}>"
     w4_dw = "_w4" if bf16 and w.n_tokens >= 1024 else ""
+    w4_dh = "_w4" if bf16 and min(w.strip or w.vocab, w.vocab) >= 1024 else ""
     kernels = {
         "strip_lse": "lce::strip_lse_kernel" + w4,
         "merge": "lce::fold_kernel",
         "strip_grad": "lce::strip_grad_kernel" + w4,
-        "gemm_dh": "lce::gemm_f32out_kernel<A K-contig, B MN-contig>",
+        "gemm_dh": f"lce::gemm_f32out_kernel{w4_dh}<A K-contig, B MN-contig>",
         "gemm_dw": f"lce::gemm_f32out_kernel{w4_dw}<A MN-contig, B MN-contig>",
         "gemm_dh_dw": f"lce::gemm_dh_dw_kernel{w4_dw} (dH and dW sharing one launch)",
     }

@@ -770,9 +770,8 @@ __device__ __forceinline__ void gemm_epilogue_w4(const GemmArgs<T>& g, w4::Acc& 
   }
 }
 
-// dW (blocked G and h, both MN-contiguous) on the one-wave-per-SIMD engine;
-// AK = true is dH (K-contiguous blocked G, MN-contiguous W_s), which only the
-// shared launch below runs on it.
+// dH (AK: K-contiguous blocked G, MN-contiguous W_s) and dW (blocked G and
+// h, both MN-contiguous) on the one-wave-per-SIMD engine.
 template <bool AK, bool Accum>
 __global__ __launch_bounds__(w4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_f32out_kernel_w4(GemmArgs<__bf16> g) {
@@ -1260,12 +1259,13 @@ static hipError_t launch_gemm(GemmArgs<T> g, hipStream_t st) {
   g.m_tiles = cdiv(g.m, kTile);
   g.n_tiles = cdiv(g.n, kTile);
   g.group_m = kGemmGroupM;
-  if constexpr (std::is_same<T, __bf16>::value && !AK && !BK) {
-    // dW on the one-wave-per-SIMD engine from 16 K stages on (5-6% faster at
-    // 131072 tokens).  dH stays on the eight-wave engine: on the one-wave
-    // engine its main loop was faster but the read-modify-write epilogue,
-    // which every compute unit reaches at once and nothing overlaps, made it
-    // 0.7-1.1% slower in three same-box comparisons.
+  if constexpr (std::is_same<T, __bf16>::value && !BK) {
+    // dH and dW on the one-wave-per-SIMD engine from 16 K stages on.  dW is
+    // 5-6% faster there at 131072 tokens.  dH alone measures 0.7-1.1% slower
+    // (its read-modify-write epilogue, whose stores the next tile's first
+    // barrier waits for, costs more than its faster main loop saves), but
+    // the whole step is 0.7% faster with it there (the kernels after it run
+    // faster), so the step decides.
     if (cdiv(g.k_len, w4::kStageK) >= kW4MinStages) {
       const int64_t tiles = g.m_tiles * g.n_tiles;
       const int64_t p = persistent_blocks();
