@@ -46,17 +46,21 @@ template <> constexpr bool kGBlocked<__bf16> = true;
 // v_permlane32_swap x of the lower and of the upper half, so op of the two is
 // the xor-16 and then the xor-32 combination (the same operands, in either
 // order, as exchanges through ds_bpermute, without their LDS round trips).
-// The swaps are written as assembly: through the builtin, the optimiser
-// replaced the second result by the first in this use.  The s_nop covers the
-// wait states between the VALU write of an operand and the swap that the
-// compiler itself places before these instructions.
+// The swap's results are copied to scalars before the bit casts:
+// __builtin_bit_cast of an element of the returned vector read element 0
+// for either index.
+__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+
 template <typename Op>
 __device__ __forceinline__ float combine_row_groups(float x, Op op) {
-  float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  float c = op(a, b), d = c;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
-  return op(c, d);
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t p0 = p[0], p1 = p[1];
+  x = op(as_float(p0), as_float(p1));
+  const uint32_t w = __builtin_bit_cast(uint32_t, x);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  const uint32_t q0 = q[0], q1 = q[1];
+  return op(as_float(q0), as_float(q1));
 }
 
 // The token of column block ni of a tile that this lane's values belong to.
