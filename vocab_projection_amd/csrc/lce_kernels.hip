@@ -12,8 +12,13 @@
 //
 // Backward, per strip: strip_grad recomputes Z^T and writes
 // G = scale * (softmax - onehot) as the input element type into the strip
-// buffer [N, ldG]; gemm_dh forms dH (+)= G . W_s and gemm_dw forms
-// dW_s = G^T . h, both accumulating in fp32.
+// buffer [N, ldG] (bf16: in blocks of 16 tokens); gemm_dh forms
+// dH (+)= G . W_s and gemm_dw forms dW_s = G^T . h, both accumulating in
+// fp32 (one shared launch where that is shorter).
+//
+// The bf16 GEMMs with at least 16 K stages of 64 run on the one-wave-per-SIMD
+// engine (tile_engine_w4.h), the rest on the eight-wave engine
+// (tile_engine.h).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -165,9 +170,7 @@ __device__ __forceinline__ void lse_epilogue(const StripArgs<T>& a, AccT& acc, i
   }
 }
 
-// The forward strip on the one-wave-per-SIMD engine (bf16); Late: the copy
-// schedule of w4::run_tiles for blocks with many tiles.
-template <bool Late>
+// The forward strip on the one-wave-per-SIMD engine (bf16).
 __global__ __launch_bounds__(w4::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void strip_lse_kernel_w4(StripArgs<__bf16> a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -175,7 +178,7 @@ void strip_lse_kernel_w4(StripArgs<__bf16> a) {
   const Operand<__bf16> B{a.hidden, a.H, a.N, a.H};
   const TileGrid grid{a.m_tiles, a.n_tiles, a.group_m, blockIdx.x, gridDim.x, true};
   int32_t tgt[w4::kNI];  // loaded at a tile's start, used by its epilogue
-  w4::run_tiles<w4::KRow128, w4::KRow128, Late>(
+  w4::run_tiles<w4::KRow128, w4::KRow128>(
       A, B, a.H, grid, lds,
       [&](int64_t, int64_t n0) { lse_targets<__bf16, w4::Acc>(a, n0, tgt); },
       [&](w4::Acc& acc, int64_t m0, int64_t n0, char*) { lse_epilogue(a, acc, m0, n0, tgt); });
@@ -1233,7 +1236,7 @@ hipError_t launch_strip_lse(StripArgs<T> a, hipStream_t st) {
   a.n_tiles = cdiv(a.N, kTile);
   a.group_m = kStripGroupM;
   if constexpr (std::is_same<T, __bf16>::value)
-    if (use_w4(a)) return launch_w4(strip_lse_kernel_w4<false>, nullptr, a, st);
+    if (use_w4(a)) return launch_w4(strip_lse_kernel_w4, nullptr, a, st);
   const int64_t blocks = grid_blocks(a.m_tiles * a.n_tiles, stages_of<T>(a.H));
   if (!grid_ok(blocks)) return hipErrorInvalidConfiguration;
   hipError_t e = set_lds<T>(reinterpret_cast<const void*>(&strip_lse_kernel<T>));

@@ -1,5 +1,6 @@
 // tile_engine_w4.h - the 256x256 MFMA tile of C = A . B^T with one wave per
-// SIMD (gfx950), for two K-contiguous bf16 operands.
+// SIMD (gfx950), for bf16 operands: K-contiguous ones in rows of 128 bytes
+// (KRow128), or any layout of the eight-wave engine through Pair.
 //
 // A block of 256 threads: four wave64s in a 2x2 grid, one per SIMD, each
 // owning a 128x128 sub-tile of fp32 accumulators (8 x 8 MFMA tiles of
