@@ -247,11 +247,11 @@ def kernel_breakdown(args, B, torch, w, p, h, W, t, lse, dh, dw, go, ws, order, 
     strip_lse launch over the whole vocabulary when it fits), and each strip of
     the backward runs strip_grad, then dH and dW as two launches or as the one
     shared launch that lce_backward_fold makes for that strip."""
-    # bf16 GEMMs with K >= 1024 run on the one-wave-per-SIMD engine: the strip
-    # kernels (K = H), dH (K = strip rows), dW (K = tokens) and the shared
-    # dH + dW launch
+    # bf16 GEMMs run on the one-wave-per-SIMD engine from K >= 768 (the strip
+    # kernels, K = H) or K >= 1024 (dH, K = strip rows; dW, K = tokens; the
+    # shared dH + dW launch)
     bf16 = w.dtype == "bf16"
-    w4 = "_w4" if bf16 and w.hidden >= 1024 else f"<{'bf16' if bf16 else 'float'}>"
+    w4 = "_w4" if bf16 and w.hidden >= 768 else f"<{'bf16' if bf16 else 'float'}>"
     w4_dw = "_w4" if bf16 and w.n_tokens >= 1024 else ""
     w4_dh = "_w4" if bf16 and min(w.strip or w.vocab, w.vocab) >= 1024 else ""
     kernels = {

@@ -170,6 +170,9 @@ SMALL = [
     # at least 8 tiles per block (17 x 122 tiles in one strip): the gradient
     # strip's late copy schedule
     S.small("bf16_w4_late_copies", 4160, 1024, 31000, 31000, ignore_frac=0.1),
+    # the one-wave strip kernels at their threshold: H = 776, 13 K stages with
+    # a tail of 8 elements
+    S.small("bf16_w4_h776", 700, 776, 2600, 1024, ignore_frac=0.1),
     # the one-wave dH and dW (and their shared launch) with H = 1160, a ragged
     # output tile of 136 columns, and 2100 tokens, a K tail of 52
     S.small("bf16_w4_ragged_h", 2100, 1160, 3001, 2048, ignore_frac=0.1),

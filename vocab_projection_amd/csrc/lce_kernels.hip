@@ -1214,18 +1214,22 @@ static hipError_t launch_w4(void (*early)(StripArgs<__bf16>), void (*late)(Strip
   return hipGetLastError();
 }
 
-// bf16 strips of at least 16 K stages (H >= 1024) run on the one-wave-per-SIMD
-// engine; shorter ones, and fp32, on the eight-wave engine.  With a single
-// wave on a SIMD nothing covers a tile's epilogue, which the MFMAs of 16
-// stages amortise and those of 8 do not: at H = 512 the one-wave forward took
-// 11% longer than the eight-wave one, at H = 2048 it was 1.5% slower at 4096
-// tokens and 4% faster at 131072, at H = 6144 5% faster.
+// bf16 strip kernels of at least 12 K stages (H >= 768), and output GEMMs of
+// at least 16, run on the one-wave-per-SIMD engine; shorter ones, and fp32,
+// on the eight-wave engine.  With a single wave on a SIMD nothing covers a
+// tile's epilogue, which the MFMAs of 12 stages amortise and those of 8 do
+// not: at H = 512 the one-wave forward took 11% longer than the eight-wave
+// one; with the one-wave strip kernels the step was 1.6% faster at H = 768,
+// 0.5% at 1024 and 2.6% at 1536 (32768 tokens), and at H = 2048 the forward
+// 4% faster at 131072 tokens.  The output GEMMs' read-modify-write epilogue
+// weighs more per tile, and they keep 16.
+constexpr int64_t kW4MinStagesStrip = 12;
 constexpr int64_t kW4MinStages = 16;
 
 template <typename T>
 static bool use_w4(const StripArgs<T>& a) {
   if constexpr (std::is_same<T, __bf16>::value)
-    return cdiv(a.H, w4::kStageK) >= kW4MinStages;
+    return cdiv(a.H, w4::kStageK) >= kW4MinStagesStrip;
   else
     return false;
 }
